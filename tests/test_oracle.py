@@ -1,0 +1,368 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test checks the oracle against something other than itself: a closed
+form, an invariant of softmax attention, brute force, a library routine
+(torch's scaled_dot_product_attention in float64 on the CPU) or the geometry
+the pages print (tests/golden/gemma4_geometry.txt).  The cases are chosen so
+that a dropped term, a wrong sign or index, a transposed operand or an
+off-by-one in the mask fails at least one of them.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attn64 as O
+from decode_attention_gemma_amd import workloads as W
+from conftest import read_golden
+
+RNG = np.random.default_rng(7)
+
+
+def _desc(nq, nkv, d, window=0, keqv=0, owner=-1, scale=None):
+    return W.LayerDesc(nq, nkv, d, window, keqv, owner, scale if scale is not None else 1 / math.sqrt(d))
+
+
+# --------------------------------------------------------------------------
+# attend(): closed forms and invariants
+# --------------------------------------------------------------------------
+
+def test_single_key_returns_its_value_exactly():
+    D = 16
+    q, K, V = RNG.normal(size=D), RNG.normal(size=(1, D)), RNG.normal(size=(1, D))
+    assert np.array_equal(O.attend(q, K, V, 0.37), V[0])
+
+
+def test_zero_query_gives_mean_of_values():
+    D, n = 8, 11
+    K, V = RNG.normal(size=(n, D)), RNG.normal(size=(n, D))
+    np.testing.assert_allclose(O.attend(np.zeros(D), K, V, 1.0), V.mean(axis=0), rtol=0, atol=1e-14)
+
+
+def test_two_keys_closed_form():
+    # s = scale * K q = [1, 0]  ->  weights e/(1+e), 1/(1+e)
+    q = np.array([1.0, 0.0])
+    K = np.array([[2.0, 0.0], [0.0, 5.0]])
+    V = np.array([[1.0, 0.0], [0.0, 1.0]])
+    e = math.e
+    np.testing.assert_allclose(O.attend(q, K, V, 0.5), [e / (1 + e), 1 / (1 + e)], rtol=1e-15)
+
+
+def test_weights_follow_exponential_ratios():
+    # V = identity exposes the weights: w_i / w_j = exp(scale (s_i - s_j)), sum 1.
+    D = n = 6
+    q, K = RNG.normal(size=D), RNG.normal(size=(n, D))
+    scale = 0.7
+    w = O.attend(q, K, np.eye(n), scale)
+    assert abs(w.sum() - 1) < 1e-14 and (w > 0).all()
+    s = K @ q
+    for i in range(n):
+        for j in range(n):
+            assert abs(w[i] / w[j] - math.exp(scale * (s[i] - s[j]))) < 1e-12 * max(1, w[i] / w[j])
+
+
+def test_scale_multiplies_logits():
+    D, n = 8, 9
+    q, K, V = RNG.normal(size=D), RNG.normal(size=(n, D)), RNG.normal(size=(n, D))
+    np.testing.assert_allclose(O.attend(q, K, V, 0.25), O.attend(0.25 * q, K, V, 1.0), atol=1e-14)
+    # a huge scale tends to the arg-max row
+    k = int(np.argmax(K @ q))
+    np.testing.assert_allclose(O.attend(q, K, V, 1e4), V[k], atol=1e-9)
+
+
+def test_shift_of_all_keys_leaves_output_unchanged():
+    D, n = 8, 13
+    q, K, V = RNG.normal(size=D), RNG.normal(size=(n, D)), RNG.normal(size=(n, D))
+    c = RNG.normal(size=D)
+    np.testing.assert_allclose(O.attend(q, K + c, V, 0.5), O.attend(q, K, V, 0.5), atol=1e-13)
+
+
+def test_constant_values_give_that_value():
+    D, n = 8, 5
+    v = RNG.normal(size=D)
+    out = O.attend(RNG.normal(size=D), RNG.normal(size=(n, D)), np.tile(v, (n, 1)), 1.0)
+    np.testing.assert_allclose(out, v, atol=1e-14)
+
+
+def test_attend_matches_per_key_loop():
+    D, n = 5, 7
+    q, K, V = RNG.normal(size=D), RNG.normal(size=(n, D)), RNG.normal(size=(n, 3))
+    scores = [0.3 * sum(q[d] * K[k][d] for d in range(D)) for k in range(n)]
+    m = max(scores)
+    ws = [math.exp(s - m) for s in scores]
+    ref = [sum(ws[k] * V[k][j] for k in range(n)) / sum(ws) for j in range(3)]
+    np.testing.assert_allclose(O.attend(q, K, V, 0.3), ref, atol=1e-14)
+
+
+def test_no_keys_gives_zeros():
+    assert np.array_equal(O.attend(np.ones(4), np.zeros((0, 4)), np.zeros((0, 4)), 1.0), np.zeros(4))
+    out = O.decode_sequence(_desc(2, 1, 4), np.ones((2, 4)), np.zeros((1, 0, 4)), None, 0)
+    assert np.array_equal(out, np.zeros((2, 4)))
+
+
+def test_large_scores_do_not_overflow():
+    D, n = 16, 4
+    q = np.full(D, 64.0)
+    K = np.vstack([np.full(D, 64.0), -np.full(D, 64.0), np.zeros(D), np.full(D, 63.0)])
+    V = RNG.normal(size=(n, D))
+    out = O.attend(q, K, V, 1.0)
+    assert np.isfinite(out).all()
+    np.testing.assert_allclose(out, V[0], atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# key ranges: sliding window / causal mask
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("window", [0, 1, 2, 8, 1024])
+def test_key_range_counts(window):
+    for n_keys in (1, 5, 17, 48):
+        for p in range(n_keys):
+            lo, hi = O.key_range(p, n_keys, window)
+            assert hi == p + 1  # causal: own key is the newest visible
+            expect = p + 1 if window == 0 else min(window, p + 1)
+            assert hi - lo == expect
+
+
+def test_key_range_past_the_end_and_empty():
+    assert O.key_range(10, 4, 0) == (0, 4)
+    assert O.key_range(10, 4, 3) == (4, 4)  # window starts after the last key: empty
+    assert O.key_range(-1, 4, 0) == (0, 0)
+
+
+def _seq(n_kv, n, D):
+    return RNG.normal(size=(n_kv, n, D)), RNG.normal(size=(n_kv, n, D))
+
+
+def test_window_one_returns_own_value():
+    d = _desc(4, 2, 8, window=1)
+    K, V = _seq(2, 9, 8)
+    out = O.decode_sequence(d, RNG.normal(size=(4, 8)), K, V, 9)
+    for h in range(4):
+        np.testing.assert_array_equal(out[h], V[h // 2, 8])
+
+
+def test_sliding_equals_global_when_window_covers_context():
+    K, V = _seq(2, 20, 8)
+    q = RNG.normal(size=(4, 8))
+    a = O.decode_sequence(_desc(4, 2, 8, window=20), q, K, V, 20)
+    b = O.decode_sequence(_desc(4, 2, 8, window=0), q, K, V, 20)
+    np.testing.assert_array_equal(a, b)
+    c = O.decode_sequence(_desc(4, 2, 8, window=19), q, K, V, 20)
+    assert not np.allclose(b, c)
+
+
+@pytest.mark.parametrize("W", [1, 3, 8])
+def test_window_boundary_by_perturbation(W):
+    L, D = 17, 8
+    d = _desc(2, 1, D, window=W)
+    K, V = _seq(1, L, D)
+    q = RNG.normal(size=(2, D))
+    base = O.decode_sequence(d, q, K, V, L)
+    p = L - 1
+    outside, inside = p - W, p - W + 1
+    if outside >= 0:
+        K2, V2 = K.copy(), V.copy()
+        K2[0, outside] += 5.0
+        V2[0, outside] += 5.0
+        np.testing.assert_array_equal(O.decode_sequence(d, q, K2, V2, L), base)
+    V3 = V.copy()
+    V3[0, inside] += 5.0
+    assert not np.allclose(O.decode_sequence(d, q, K, V3, L), base)
+    # and nothing newer than the query exists in decode: extra rows are ignored
+    K4 = np.concatenate([K, RNG.normal(size=(1, 3, D))], axis=1)
+    V4 = np.concatenate([V, RNG.normal(size=(1, 3, D))], axis=1)
+    np.testing.assert_array_equal(O.decode_sequence(d, q, K4, V4, L), base)
+
+
+# --------------------------------------------------------------------------
+# grouping, k_eq_v, positions offset
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nq,nkv", [(4, 2), (8, 2), (16, 8), (16, 1), (4, 1)])
+def test_gqa_equals_mha_with_contiguously_repeated_kv(nq, nkv):
+    D, L = 8, 12
+    K, V = _seq(nkv, L, D)
+    q = RNG.normal(size=(nq, D))
+    G = nq // nkv
+    gqa = O.decode_sequence(_desc(nq, nkv, D, window=5), q, K, V, L)
+    mha = O.decode_sequence(_desc(nq, nq, D, window=5), q, np.repeat(K, G, axis=0),
+                            np.repeat(V, G, axis=0), L)
+    np.testing.assert_array_equal(gqa, mha)
+    if nkv > 1:  # an interleaved (h mod n_kv) grouping would differ
+        inter = O.decode_sequence(_desc(nq, nq, D, window=5), q, np.tile(K, (G, 1, 1)),
+                                  np.tile(V, (G, 1, 1)), L)
+        assert not np.allclose(gqa, inter)
+
+
+def test_k_eq_v_equals_passing_k_as_v():
+    K, _ = _seq(1, 10, 16)
+    q = RNG.normal(size=(4, 16))
+    a = O.decode_sequence(_desc(4, 1, 16, keqv=1), q, K, None, 10)
+    b = O.decode_sequence(_desc(4, 1, 16, keqv=0), q, K, K, 10)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_rows_given_from_an_offset_position():
+    d = _desc(4, 2, 8, window=6)
+    K, V = _seq(2, 30, 8)
+    q = RNG.normal(size=(4, 8))
+    full = O.decode_sequence(d, q, K, V, 30)
+    part = O.decode_sequence(d, q, K[:, 24:], V[:, 24:], 30, k_pos0=24)
+    np.testing.assert_array_equal(full, part)
+    with pytest.raises(O.OracleError):
+        O.decode_sequence(d, q, K[:, 25:], V[:, 25:], 30, k_pos0=25)
+
+
+# --------------------------------------------------------------------------
+# prefill vs decode, causality
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("window,start", [(0, 0), (0, 7), (5, 9), (16, 3)])
+def test_prefill_rows_equal_decode_at_each_position(window, start):
+    T, D = 6, 8
+    d = _desc(4, 2, D, window=window)
+    K, V = _seq(2, start + T, D)
+    q = RNG.normal(size=(T, 4, D))
+    pre = O.prefill_sequence(d, q, K, V, start)
+    for t in range(T):
+        dec = O.decode_sequence(d, q[t], K, V, start + t + 1)
+        np.testing.assert_array_equal(pre[t], dec)
+
+
+def test_prefill_is_causal():
+    T, D, start = 5, 8, 4
+    d = _desc(2, 1, D)
+    K, V = _seq(1, start + T, D)
+    q = RNG.normal(size=(T, 2, D))
+    base = O.prefill_sequence(d, q, K, V, start)
+    V2 = V.copy()
+    V2[0, start + 2] += 3.0  # visible to tokens 2.. only
+    out = O.prefill_sequence(d, q, K, V2, start)
+    np.testing.assert_array_equal(out[:2], base[:2])
+    assert not np.allclose(out[2:], base[2:])
+
+
+# --------------------------------------------------------------------------
+# whole layers against a library routine
+# --------------------------------------------------------------------------
+
+def _sdpa(q, K, V, qpos, window, scale, nq, nkv):
+    """torch SDPA in float64 on the CPU with an explicit boolean mask."""
+    G = nq // nkv
+    Kr = torch.from_numpy(np.repeat(K, G, axis=0))  # [nq, n, D]
+    Vr = torch.from_numpy(np.repeat(V, G, axis=0))
+    n = K.shape[1]
+    kp = np.arange(n)[None, :]
+    qp = np.asarray(qpos)[:, None]
+    ok = (kp <= qp) & ((qp - kp < window) if window > 0 else True)
+    mask = torch.from_numpy(np.broadcast_to(ok, (len(qpos), n)).copy())
+    qt = torch.from_numpy(q)  # [nq, T, D]
+    return torch.nn.functional.scaled_dot_product_attention(
+        qt, Kr, Vr, attn_mask=mask, scale=scale).numpy()
+
+
+@pytest.mark.parametrize("nq,nkv,D,window,keqv", [(4, 2, 32, 8, 0), (4, 1, 64, 0, 1),
+                                                   (16, 8, 16, 5, 0), (16, 1, 32, 0, 1)])
+def test_prefill_matches_torch_sdpa_fp64(nq, nkv, D, window, keqv):
+    start, T = 9, 7
+    K, V = _seq(nkv, start + T, D)
+    if keqv:
+        V = K
+    q = RNG.normal(size=(T, nq, D))
+    d = _desc(nq, nkv, D, window=window, keqv=keqv, scale=0.3)
+    ours = O.prefill_sequence(d, q, K, None if keqv else V, start)
+    ref = _sdpa(q.transpose(1, 0, 2), K, V, start + np.arange(T), window, 0.3, nq, nkv)
+    np.testing.assert_allclose(ours, ref.transpose(1, 0, 2), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# owner resolution
+# --------------------------------------------------------------------------
+
+def test_owner_resolution_explicit_and_self():
+    L = [_desc(8, 2, 16, 4), _desc(8, 2, 16, 0), _desc(8, 2, 16, 4, owner=2),
+         _desc(4, 2, 16, 4, owner=0), _desc(8, 2, 16, 0, owner=1)]
+    assert O.resolve_owners(L) == [0, 1, 2, 0, 1]
+
+
+@pytest.mark.parametrize("case", ["later", "self_chain", "geometry", "window", "keqv", "negative"])
+def test_owner_resolution_rejects(case):
+    base = [_desc(8, 2, 16, 4), _desc(8, 2, 16, 4, owner=0), _desc(8, 2, 16, 4)]
+    if case == "later":
+        base[0] = _desc(8, 2, 16, 4, owner=2)
+    elif case == "self_chain":
+        base[2] = _desc(8, 2, 16, 4, owner=1)
+    elif case == "geometry":
+        base[2] = _desc(8, 4, 16, 4, owner=0)
+    elif case == "window":
+        base[2] = _desc(8, 2, 16, 0, owner=0)
+    elif case == "keqv":
+        base[2] = _desc(8, 2, 16, 4, keqv=1, owner=0)
+    elif case == "negative":
+        base[2] = _desc(8, 2, 16, 4, owner=-3)
+    with pytest.raises(O.OracleError):
+        O.resolve_owners(base)
+
+
+def test_shared_reader_sees_owner_cache_with_its_own_query_and_scale():
+    # the reader's output is the owner's K/V attended with the reader's q,
+    # its own scale and its own (equal) window
+    D = 8
+    owner, reader = _desc(4, 2, D, 6), _desc(8, 2, D, 6, owner=0, scale=0.9)
+    assert O.resolve_owners([owner, reader]) == [0, 0]
+    K, V = _seq(2, 15, D)
+    q = RNG.normal(size=(8, D))
+    got = O.decode_sequence(reader, q, K, V, 15)
+    for h in range(8):
+        ref = _sdpa(q[h][None, None, :], K[h // 4:h // 4 + 1], V[h // 4:h // 4 + 1], [14], 6, 0.9, 1, 1)
+        np.testing.assert_allclose(got[h], ref[0, 0], atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# workload geometry against the pages
+# --------------------------------------------------------------------------
+
+def test_workload_geometry_matches_pages():
+    g = read_golden("gemma4_geometry.txt")
+    v = {k: int(val) for k, (val, _) in g.items()}
+    wl = W.g12b_decode()
+    assert wl.n_layers == v["12b.n_layers"]
+    sl = [d for d in wl.layers if d.window > 0]
+    gl = [d for d in wl.layers if d.window == 0]
+    assert sl and gl
+    for d in sl:
+        assert (d.n_q_heads, d.n_kv_heads, d.head_dim, d.window) == (
+            v["12b.sliding.n_q_heads"], v["12b.sliding.n_kv_heads"], v["12b.sliding.head_dim"],
+            v["12b.sliding.window"])
+        assert d.k_eq_v == 0
+    for d in gl:
+        assert (d.n_kv_heads, d.head_dim, d.k_eq_v) == (
+            v["12b.global.n_kv_heads"], v["12b.global.head_dim"], v["12b.global.k_eq_v"])
+    assert len(wl.layers) - len(wl.owner_layers()) == v["12b.kv_shared_layers"]
+    assert W.g12b_prefill(960).n_tok == v["12b.prefill_bucket"]
+    e4 = W.e4b_decode()
+    for d in e4.layers:
+        assert (d.n_q_heads, d.n_kv_heads, d.head_dim) == (
+            v["e4b.n_q_heads"], v["e4b.n_kv_heads"], v["e4b.head_dim"])
+        assert d.window in (0, v["e4b.window"])
+    assert (len(e4.owner_layers()) < e4.n_layers) == bool(v["e4b.kv_sharing"])
+    # tensor-parallel per-rank shapes quoted on the pages (TP = 2)
+    tp = 2
+    nkv = v["e4b.n_kv_heads"]
+    assert (nkv // tp if nkv % tp == 0 else nkv) == v["tp2.e4b.kv_heads_per_rank"]
+    assert (v["12b.sliding.n_q_heads"] // tp) // v["12b.global.n_kv_heads"] == \
+        v["tp2.12b.global.groups_per_rank"]
+
+
+def test_owner_tables_of_shared_stacks():
+    # the most recent earlier owner of the same attention type (hand-derived)
+    e4 = W.e4b_decode()
+    assert [e4.owner(i) for i in range(12)] == [0, 1, 2, 3, 4, 5, 4, 4, 4, 4, 4, 5]
+    assert O.resolve_owners(e4.layers) == [0, 1, 2, 3, 4, 5, 4, 4, 4, 4, 4, 5]
+    lc = W.long_decode()
+    expect = list(range(20)) + [17 if i % 6 == 5 else 19 for i in range(20, 48)]
+    assert O.resolve_owners(lc.layers) == expect
+    assert O.resolve_owners(W.g12b_decode().layers) == list(range(48))
