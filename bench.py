@@ -1,0 +1,279 @@
+"""Benchmark: Gemma-4 12B-shaped attention over a device-resident KV cache.
+
+One step = one pass of the layer stack: the 48 per-layer g4attn_decode calls
+of the 12B-shaped decode stack (B = 16, context U{1024..4096}), captured once
+into a HIP graph and replayed.  `value` is the KV bytes the step must read
+(visible keys x KV heads x head_dim x 2 bytes, K and V, V counted once more
+only on layers that have a V plane) divided by the step time, in GB/s.
+
+Also reported on the same line:
+  roofline      the dominant kernel (sliding-layer decode, head_dim 256),
+                timed over a graph of the 40 sliding-layer launches;
+  prefill       the 12B-shaped 64-token prefill chunk stack (B = 4) after
+                960 and 4032 cached tokens, in TFLOP/s of visible-pair work;
+  cpu_baseline  the fp64 oracle on a bounded sample of the same decode
+                workload, on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-prefill] [--long]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "decode-attn KV-read GB/s (% HBM peak) + prefill TFLOP/s, 12B shape, 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kv_bytes(wl, layer):
+    """Algorithmic KV bytes one decode call of `layer` reads."""
+    d = wl.layers[layer]
+    keys = 0
+    for L in wl.seq_lens:
+        keys += min(L, d.window) if d.window > 0 else L
+    return keys * d.n_kv_heads * d.head_dim * 2 * (1 if d.k_eq_v else 2)
+
+
+def prefill_flops(wl, layer):
+    """Visible (query, key) pairs x 4 x head_dim, over all query heads."""
+    d = wl.layers[layer]
+    pairs = 0
+    for s in wl.start_pos:
+        for t in range(wl.n_tok):
+            p = s + t
+            lo = max(0, p - d.window + 1) if d.window > 0 else 0
+            pairs += p + 1 - lo
+    return pairs * d.n_q_heads * 4 * d.head_dim
+
+
+def graph_of(fn, stream):
+    import torch
+
+    with torch.cuda.stream(stream):
+        fn()  # warm-up launch on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    return g
+
+
+def time_graph(g, warmup, reps):
+    """Mean ms per replay; replays run on the current stream, where the
+    events are recorded too."""
+    import torch
+
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for _ in range(reps):
+        g.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_decode(args, stream):
+    import torch
+
+    from decode_attention_gemma_amd import harness as H, workloads as W
+
+    wl = W.g12b_decode()
+    log(f"[bench] setup {wl.name}")
+    st = H.make_stack(wl, "cuda")
+    H.fill_cache(st, wl, "cuda")
+    bufs = H.StepBuffers(wl, "cuda")
+    step_graph = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream), stream)
+    log(f"[bench] decode step: {args.warmup} warm-up, {args.steps} timed replays")
+    t0 = time.perf_counter()
+    ms = time_graph(step_graph, args.warmup, args.steps)
+    wall = time.perf_counter() - t0
+    step_bytes = sum(kv_bytes(wl, i) for i in range(wl.n_layers))
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    log(f"[bench] decode step {ms*1e3:.1f} us, {gbs:.0f} GB/s (wall incl. warm-up {wall:.2f} s)")
+
+    # dominant kernel: the sliding-layer decode (head_dim 256), one launch per
+    # sliding layer so every launch streams a different cache region
+    sliding = [i for i in range(wl.n_layers) if wl.layers[i].window > 0]
+    dom_graph = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream, layers=sliding),
+                         stream)
+    dom_ms = time_graph(dom_graph, 3, max(args.steps, 10)) / len(sliding)
+    dom_bytes = kv_bytes(wl, sliding[0])
+    dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+    log(f"[bench] sliding decode kernel {dom_ms*1e3:.1f} us/launch, {dom_gbs:.0f} GB/s")
+    glob = [i for i in range(wl.n_layers) if wl.layers[i].window == 0]
+    glob_graph = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream, layers=glob),
+                          stream)
+    glob_ms = time_graph(glob_graph, 3, max(args.steps, 10)) / len(glob)
+    glob_gbs = kv_bytes(wl, glob[0]) / (glob_ms * 1e-3) / 1e9
+    log(f"[bench] global decode kernel {glob_ms*1e3:.1f} us/launch, {glob_gbs:.0f} GB/s")
+    out = {
+        "wl": wl, "st": st, "bufs": bufs, "ms": ms, "step_bytes": step_bytes, "gbs": gbs,
+        "dom": {"ms": dom_ms, "bytes": dom_bytes, "gbs": dom_gbs},
+        "glob": {"ms": glob_ms, "bytes": kv_bytes(wl, glob[0]), "gbs": glob_gbs},
+    }
+    return out
+
+
+def bench_prefill(prefix, args, stream):
+    import torch
+
+    from decode_attention_gemma_amd import harness as H, workloads as W
+
+    wl = W.g12b_prefill(prefix)
+    log(f"[bench] setup {wl.name}")
+    st = H.make_stack(wl, "cuda")
+    H.fill_cache(st, wl, "cuda")
+    bufs = H.StepBuffers(wl, "cuda")
+    g = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream), stream)
+    ms = time_graph(g, args.warmup, args.steps)
+    flops = sum(prefill_flops(wl, i) for i in range(wl.n_layers))
+    tf = flops / (ms * 1e-3) / 1e12
+    glob = [i for i in range(wl.n_layers) if wl.layers[i].window == 0]
+    gg = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream, layers=glob), stream)
+    gms = time_graph(gg, 2, max(args.steps, 5)) / len(glob)
+    gtf = prefill_flops(wl, glob[0]) / (gms * 1e-3) / 1e12
+    log(f"[bench] prefill P={prefix}: {ms*1e3:.1f} us/step, {tf:.1f} TFLOP/s; "
+        f"global layer {gms*1e3:.1f} us, {gtf:.1f} TFLOP/s")
+    del st, bufs, g, gg
+    torch.cuda.empty_cache()
+    return {"us_per_step": round(ms * 1e3, 2), "tflops": round(tf, 2),
+            "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4), "gflop_per_step": round(flops / 1e9, 2),
+            "global_layer_us": round(gms * 1e3, 2), "global_layer_tflops": round(gtf, 2)}
+
+
+def cpu_baseline(dec):
+    """The fp64 oracle on the same decode workload, layer by layer (inputs are
+    copied to the host and widened to fp64 outside the timed region)."""
+    import numpy as np
+    import torch
+
+    from decode_attention_gemma_amd import workloads as W
+    from oracle import attn64 as O
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    wl, bufs = dec["wl"], dec["bufs"]
+    cores = len(os.sched_getaffinity(0))
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    log(f"[bench] cpu baseline: fp64 oracle, all {wl.n_layers} layers x {wl.batch} sequences")
+    dt = 0.0
+    nbytes = 0
+    for layer in range(wl.n_layers):
+        d = wl.layers[layer]
+        o = wl.owner(layer)
+        q = bufs.q[layer].to("cpu", torch.float64).numpy()
+        inputs = []
+        for b in range(wl.batch):
+            pos0, _ = W.kv_span(wl, o, b)
+            K = W.kv_rows(wl, o, b, "k", "cuda").to("cpu", torch.float64).numpy()
+            V = None if d.k_eq_v else W.kv_rows(wl, o, b, "v", "cuda").to("cpu", torch.float64).numpy()
+            inputs.append((q[b], K, V, wl.seq_lens[b], pos0))
+            L = wl.seq_lens[b]
+            keys = min(L, d.window) if d.window > 0 else L
+            nbytes += keys * d.n_kv_heads * d.head_dim * 2 * (1 if d.k_eq_v else 2)
+        t0 = time.perf_counter()
+        for qb, K, V, L, pos0 in inputs:
+            O.decode_sequence(d, qb, K, V, L, k_pos0=pos0)
+        dt += time.perf_counter() - t0
+        del inputs
+    if ctx is not None:
+        ctx.restore_original_limits()
+    gbs = nbytes / dt / 1e9
+    log(f"[bench] cpu baseline {dt:.2f} s for {nbytes/1e9:.3f} GB -> {gbs:.3f} GB/s")
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"one full step of the same workload (48 layers x 16 sequences, "
+                      f"{nbytes/1e9:.2f} GB of bf16 KV), fp64 numpy oracle, compute timed "
+                      f"{dt:.1f} s, BLAS threads limited to the {cores} cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention path here runs on a single "
+              "MI355X (see DESIGN.md for how it would shard); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from decode_attention_gemma_amd import g4attn
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    g4attn.load()
+    stream = torch.cuda.Stream()
+    dec = bench_decode(args, stream)
+    prefill = {}
+    if not args.no_prefill:
+        for p in (960, 4032):
+            prefill[f"prefix_{p}"] = bench_prefill(p, args, stream)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(dec)
+
+    wl = dec["wl"]
+    dom = dec["dom"]
+    line = {
+        "metric": METRIC,
+        "value": round(dec["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, no weights)",
+        "config": {
+            "workload": "12B-shaped 48-layer decode stack (40 sliding W1024 16q/8kv D256 + "
+                        "8 global 16q/1kv D512 k_eq_v), B=16, context U{1024..4096}",
+            "batch": wl.batch, "layers": wl.n_layers, "seq_lens": wl.seq_lens,
+            "kv_bytes_per_step": dec["step_bytes"],
+            "hbm_frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
+            "global_layer_decode_gbs": round(dec["glob"]["gbs"], 1),
+        },
+        "roofline": {
+            "kernel": "decode_kernel<256,false> (sliding layer)",
+            "bound": "hbm",
+            "achieved": round(dom["gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "us_per_launch": round(dom["ms"] * 1e3, 2),
+            "bytes_per_launch": dom["bytes"],
+        },
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,106 @@
+// Internal interfaces between the host plan (plan.cpp) and the HIP kernels
+// (kernels.hip).  Not part of the public ABI.
+//
+// Cache layout (per owning layer, per (sequence, KV head) segment of `cap`
+// slots, cap a multiple of 64; position p lives in slot p mod cap):
+//
+//   K plane: 16-slot blocks; a block holds head_dim/32 sub-tiles of
+//            16 keys x 32 dims = 1 KiB, each stored in the lane order of a
+//            v_mfma_f32_16x16x32_bf16 operand: lane L = key + 16 q holds
+//            dims 8q .. 8q+7 of its sub-tile's 32 (16 bytes per lane).
+//   V plane: 32-slot blocks; a block holds head_dim/16 sub-tiles of
+//            32 keys x 16 dims = 1 KiB, lane L = dim + 16 q holding the keys
+//            4q .. 4q+3 and 16+4q .. 16+4q+3 of the block (16 bytes per lane),
+//            i.e. V^T already in operand order for O^T += V^T P^T.
+//
+// so that every cache read of the kernels is a contiguous 1 KiB per wave
+// instruction.  k_eq_v layers have only the K plane.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace g4 {
+
+// Upper bound on decode key splits per (sequence, head block).
+constexpr int kMaxDecodeSplits = 64;
+// Upper bound on prefill key splits per (sequence, KV head, row block).
+constexpr int kMaxPrefillSplits = 8;
+// Query rows (token x head pairs) per prefill workgroup.
+constexpr int kPrefillRows = 64;
+
+inline int decode_block(bool k_eq_v) { return k_eq_v ? 16 : 32; }
+inline int prefill_tile(int head_dim) { return head_dim >= 512 ? 32 : 64; }
+
+// Byte offsets of element d of the K row / V row in one segment.
+__host__ __device__ inline int64_t k_elem_offset(int64_t slot, int d, int D) {
+  const int64_t blk = slot / 16, kk = slot % 16;
+  return ((blk * (D / 32) + d / 32) * 64 + ((d % 32) / 8) * 16 + kk) * 16 + (d % 8) * 2;
+}
+__host__ __device__ inline int64_t v_elem_offset(int64_t slot, int d, int D) {
+  const int64_t blk = slot / 32;
+  const int kk = (int)(slot % 32);
+  const int q = (kk % 16) / 4;
+  const int j = (kk / 16) * 4 + kk % 4;
+  return ((blk * (D / 16) + d / 16) * 64 + q * 16 + d % 16) * 16 + j * 2;
+}
+
+struct AppendArgs {
+  const uint16_t* k;  // [batch][n_new][n_kv][D]
+  const uint16_t* v;  // same, or nullptr when the layer has no V plane
+  uint16_t* kp;       // owner K plane
+  uint16_t* vp;       // owner V plane, or nullptr
+  const int32_t* start;
+  const int32_t* nvalid;  // nullable
+  int n_new, n_kv, D, cap, kv_max;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;  // [B][n_q][D]
+  const uint16_t* kp;
+  const uint16_t* vp;  // == kp when k_eq_v
+  const int32_t* seq_lens;
+  uint16_t* out;     // [B][n_q][D]
+  float* part_o;     // [B][n_q][n_splits][D]
+  float* part_ml;    // [B][n_q][n_splits][2]
+  int32_t* counters; // [B][n_kv][n_hblk]
+  int n_q, n_kv, G, n_hblk, cap, window, kv_max;
+  int split_keys, n_splits;
+  int merge_in_kernel;  // 1: last arriving workgroup merges; 0: a merge kernel follows
+  float scale_log2;     // scale * log2(e)
+};
+
+struct PrefillArgs {
+  const uint16_t* q;  // [B][T][n_q][D]
+  const uint16_t* kp;
+  const uint16_t* vp;  // == kp when k_eq_v
+  const int32_t* start_pos;
+  uint16_t* out;      // [B][T][n_q][D]
+  float* part_o;      // [B][n_kv][T*G][n_splits][D]
+  float* part_ml;     // [B][n_kv][T*G][n_splits][2]
+  int32_t* counters;  // [B][n_kv][n_rowblk]
+  int n_q, n_kv, G, T, cap, window, kv_max;
+  int rows, n_rowblk;
+  int split_keys, n_splits;
+  int merge_in_kernel;
+  float scale_log2;
+};
+
+struct MergeArgs {
+  const float* part_o;   // [rows][n_splits][D]
+  const float* part_ml;  // [rows][n_splits][2]
+  uint16_t* out;
+  int rows, n_splits, D;
+  // prefill rows are (sequence, KV head, token x head) and land at
+  // out[((b * T + t) * n_q + g * G + h) * D]; decode rows at out[row * D]
+  int prefill, T, G, n_q, n_kv, rows_per_group;
+};
+
+hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s);
+hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, int batch, hipStream_t s);
+hipError_t launch_prefill(int head_dim, bool k_eq_v, const PrefillArgs& a, int batch,
+                          hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+}  // namespace g4

@@ -1,0 +1,476 @@
+// Host side of the g4attn C ABI: descriptor validation, owner resolution,
+// cache / workspace planning, the bit-exact index hooks, and argument checks
+// before every kernel launch.  Nothing here allocates device memory.
+//
+// Owner rules follow "Porting Gemma-4 (2B / 4B / 12B) to AWS Inferentia2",
+// 2.1 (a KV-shared layer attends to an earlier layer's K/V and holds no cache;
+// only owning layers allocate one).  The resident cache of fixed capacity
+// follows section 5 of the same page.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/g4attn.h"
+#include "internal.h"
+
+struct LayerPlan {
+  g4attn_layer_desc d;
+  int owner;
+  int cap;          // slots per (sequence, KV head) of the owner's planes
+  uint64_t k_off;   // byte offset of the owner's K plane in the cache
+  uint64_t v_off;   // byte offset of the owner's V plane (== k_off when k_eq_v)
+};
+
+struct g4attn_stack {
+  std::vector<LayerPlan> L;
+  int max_batch = 0, kv_max = 0, max_chunk = 0;
+  uint64_t cache_bytes = 0;
+  uint64_t ws_ctr_off = 0, ws_ml_off = 0, ws_o_off = 0, ws_bytes = 0;
+  uint64_t ctr_count = 0, ml_floats = 0, o_floats = 0;
+  char* cache = nullptr;
+  char* ws = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int32_t ok() {
+  g_err.clear();
+  return G4ATTN_OK;
+}
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+bool head_dim_supported(int d) { return d == 32 || d == 64 || d == 128 || d == 256 || d == 512; }
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Slots per (sequence, KV head): always a multiple of 64 so that the 16- and
+// 32-slot operand blocks never straddle the ring's wrap.  Global layers keep
+// every position (kv_max rounded up); sliding layers keep a ring that holds a
+// window plus one chunk of new tokens, so its size does not grow with context.
+int layer_cap(const g4attn_layer_desc& d, int kv_max, int max_chunk) {
+  const int64_t full = ((int64_t)kv_max + 63) / 64 * 64;
+  if (d.window <= 0) return (int)full;
+  const int64_t need = (int64_t)d.window + max_chunk - 1;
+  const int64_t ring = (need + 63) / 64 * 64;
+  return (int)(ring < full ? ring : full);
+}
+
+int32_t check_layer(const g4attn_stack* st, int32_t layer) {
+  if (!st) return fail(G4ATTN_ERR_NULL, "stack is NULL");
+  if (layer < 0 || layer >= (int32_t)st->L.size())
+    return fail(G4ATTN_ERR_RANGE, "layer %d out of range [0, %zu)", layer, st->L.size());
+  return G4ATTN_OK;
+}
+
+// Decode split policy: enough workgroups to keep every CU busy with a few
+// independent waves, splits aligned to 64 positions.
+void decode_splits(int keys_max, int pairs, int wgs_per_cu, int* split_keys, int* n_splits) {
+  const int span = keys_max + 63;  // alignment slack of the first split
+  const int target_wgs = 256 * wgs_per_cu;
+  int ns = ceil_div(target_wgs, pairs);
+  if (ns > g4::kMaxDecodeSplits) ns = g4::kMaxDecodeSplits;
+  if (ns < 1) ns = 1;
+  int sk = ceil_div(ceil_div(span, ns), 64) * 64;
+  if (sk < 64) sk = 64;
+  *split_keys = sk;
+  *n_splits = ceil_div(span, sk);
+  if (*n_splits < 1) *n_splits = 1;
+}
+
+void prefill_splits(int span, int pairs, int KT, int max_splits, int* split_keys,
+                    int* n_splits) {
+  span += KT - 1;  // alignment slack of the first split
+  const int target_wgs = 512;
+  int ns = ceil_div(target_wgs, pairs);
+  int max_by_len = ceil_div(span, 2 * KT);
+  if (ns > max_by_len) ns = max_by_len;
+  if (ns > max_splits) ns = max_splits;
+  if (ns < 1) ns = 1;
+  int sk = ceil_div(ceil_div(span, ns), KT) * KT;
+  if (sk < KT) sk = KT;
+  *split_keys = sk;
+  *n_splits = ceil_div(span, sk);
+  if (*n_splits < 1) *n_splits = 1;
+}
+
+// Split results are merged by the last workgroup to arrive when the merge is
+// small; larger merges go to a separate kernel with one workgroup per row.
+constexpr int64_t kInKernelMergeBytes = 64 * 1024;
+
+}  // namespace
+
+extern "C" {
+
+const char* g4attn_last_error(void) { return g_err.c_str(); }
+
+int32_t g4attn_stack_create(const g4attn_layer_desc* layers, int32_t n_layers, int32_t max_batch,
+                            int32_t kv_max, int32_t max_chunk, g4attn_stack** out) {
+  if (!layers || !out) return fail(G4ATTN_ERR_NULL, "layers and out must be non-NULL");
+  if (n_layers <= 0) return fail(G4ATTN_ERR_DESC, "n_layers must be positive");
+  if (max_batch <= 0 || max_batch > 65535) return fail(G4ATTN_ERR_DESC, "max_batch %d", max_batch);
+  if (kv_max <= 0 || kv_max > (1 << 24)) return fail(G4ATTN_ERR_DESC, "kv_max %d", kv_max);
+  if (max_chunk <= 0 || max_chunk > 4096) return fail(G4ATTN_ERR_DESC, "max_chunk %d", max_chunk);
+
+  g4attn_stack* st = new (std::nothrow) g4attn_stack();
+  if (!st) return fail(G4ATTN_ERR_DESC, "out of host memory");
+  st->max_batch = max_batch;
+  st->kv_max = kv_max;
+  st->max_chunk = max_chunk;
+  st->L.resize(n_layers);
+
+  for (int i = 0; i < n_layers; ++i) {
+    const g4attn_layer_desc& d = layers[i];
+    int32_t rc = G4ATTN_OK;
+    if (d.n_q_heads <= 0 || d.n_kv_heads <= 0)
+      rc = fail(G4ATTN_ERR_DESC, "layer %d: head counts must be positive", i);
+    else if (d.n_q_heads % d.n_kv_heads != 0)
+      rc = fail(G4ATTN_ERR_DESC, "layer %d: n_q_heads %d not a multiple of n_kv_heads %d", i,
+                d.n_q_heads, d.n_kv_heads);
+    else if (d.n_q_heads > 4096)
+      rc = fail(G4ATTN_ERR_DESC, "layer %d: too many heads", i);
+    else if (d.window < 0)
+      rc = fail(G4ATTN_ERR_DESC, "layer %d: window %d < 0", i, d.window);
+    else if (d.k_eq_v != 0 && d.k_eq_v != 1)
+      rc = fail(G4ATTN_ERR_DESC, "layer %d: k_eq_v must be 0 or 1", i);
+    else if (!std::isfinite(d.scale))
+      rc = fail(G4ATTN_ERR_DESC, "layer %d: scale is not finite", i);
+    else if (!head_dim_supported(d.head_dim))
+      rc = fail(G4ATTN_ERR_UNSUPPORTED, "layer %d: head_dim %d not built (32/64/128/256/512)", i,
+                d.head_dim);
+    if (rc != G4ATTN_OK) {
+      delete st;
+      return rc;
+    }
+    int owner = i;
+    if (d.kv_owner_layer != -1 && d.kv_owner_layer != i) {
+      const int o = d.kv_owner_layer;
+      if (o < 0 || o >= i) {
+        delete st;
+        return fail(G4ATTN_ERR_OWNER, "layer %d: owner %d is not an earlier layer", i, o);
+      }
+      const g4attn_layer_desc& od = layers[o];
+      if (od.kv_owner_layer != -1 && od.kv_owner_layer != o) {
+        delete st;
+        return fail(G4ATTN_ERR_OWNER, "layer %d: owner %d is itself KV-shared", i, o);
+      }
+      if (od.n_kv_heads != d.n_kv_heads || od.head_dim != d.head_dim ||
+          od.k_eq_v != d.k_eq_v || od.window != d.window) {
+        delete st;
+        return fail(G4ATTN_ERR_OWNER,
+                    "layer %d: (n_kv_heads, head_dim, k_eq_v, window) differ from owner %d", i,
+                    o);
+      }
+      owner = o;
+    }
+    st->L[i].d = d;
+    st->L[i].owner = owner;
+  }
+
+  // cache planes of owning layers
+  uint64_t off = 0;
+  for (int i = 0; i < n_layers; ++i) {
+    LayerPlan& p = st->L[i];
+    if (p.owner != i) continue;
+    p.cap = layer_cap(p.d, kv_max, max_chunk);
+    const uint64_t plane =
+        (uint64_t)max_batch * p.d.n_kv_heads * (uint64_t)p.cap * p.d.head_dim * 2;
+    p.k_off = off;
+    off = align256(off + plane);
+    if (p.d.k_eq_v) {
+      p.v_off = p.k_off;
+    } else {
+      p.v_off = off;
+      off = align256(off + plane);
+    }
+  }
+  for (int i = 0; i < n_layers; ++i) {
+    LayerPlan& p = st->L[i];
+    if (p.owner == i) continue;
+    const LayerPlan& o = st->L[p.owner];
+    p.cap = o.cap;
+    p.k_off = o.k_off;
+    p.v_off = o.v_off;
+  }
+  st->cache_bytes = off;
+
+  // workspace: arrival counters, then (m, l) pairs, then partial outputs
+  uint64_t ctr = 0, ml = 0, of = 0;
+  for (int i = 0; i < n_layers; ++i) {
+    const g4attn_layer_desc& d = st->L[i].d;
+    const int G = d.n_q_heads / d.n_kv_heads;
+    const uint64_t hblk = (uint64_t)(G + 15) / 16;
+    const uint64_t rows_p = (uint64_t)max_chunk * G;
+    const uint64_t rblk = (rows_p + g4::kPrefillRows - 1) / g4::kPrefillRows;
+    const uint64_t c_d = (uint64_t)max_batch * d.n_kv_heads * hblk;
+    const uint64_t c_p = (uint64_t)max_batch * d.n_kv_heads * rblk;
+    const uint64_t r_d = (uint64_t)max_batch * d.n_q_heads * g4::kMaxDecodeSplits;
+    const uint64_t r_p = (uint64_t)max_batch * d.n_kv_heads * rows_p * g4::kMaxPrefillSplits;
+    ctr = std::max(ctr, std::max(c_d, c_p));
+    ml = std::max(ml, 2 * std::max(r_d, r_p));
+    of = std::max(of, (uint64_t)d.head_dim * std::max(r_d, r_p));
+  }
+  st->ctr_count = ctr;
+  st->ml_floats = ml;
+  st->o_floats = of;
+  st->ws_ctr_off = 0;
+  st->ws_ml_off = align256(ctr * 4);
+  st->ws_o_off = align256(st->ws_ml_off + ml * 4);
+  st->ws_bytes = align256(st->ws_o_off + of * 4);
+
+  *out = st;
+  return ok();
+}
+
+void g4attn_stack_destroy(g4attn_stack* stack) { delete stack; }
+
+int32_t g4attn_cache_bytes(const g4attn_stack* st, uint64_t* bytes) {
+  if (!st || !bytes) return fail(G4ATTN_ERR_NULL, "stack and bytes must be non-NULL");
+  *bytes = st->cache_bytes;
+  return ok();
+}
+
+int32_t g4attn_workspace_bytes(const g4attn_stack* st, uint64_t* bytes) {
+  if (!st || !bytes) return fail(G4ATTN_ERR_NULL, "stack and bytes must be non-NULL");
+  *bytes = st->ws_bytes;
+  return ok();
+}
+
+int32_t g4attn_bind(g4attn_stack* st, void* cache, void* workspace) {
+  if (!st || !cache || !workspace)
+    return fail(G4ATTN_ERR_NULL, "stack, cache and workspace must be non-NULL");
+  if (((uintptr_t)cache & 255) || ((uintptr_t)workspace & 255))
+    return fail(G4ATTN_ERR_RANGE, "cache and workspace must be 256-byte aligned");
+  st->cache = static_cast<char*>(cache);
+  st->ws = static_cast<char*>(workspace);
+  return ok();
+}
+
+int32_t g4attn_resolve_owner(const g4attn_stack* st, int32_t layer, int32_t* owner) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  if (!owner) return fail(G4ATTN_ERR_NULL, "owner is NULL");
+  *owner = st->L[layer].owner;
+  return ok();
+}
+
+int32_t g4attn_layer_capacity(const g4attn_stack* st, int32_t layer, int32_t* cap) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  if (!cap) return fail(G4ATTN_ERR_NULL, "cap is NULL");
+  *cap = st->L[layer].cap;
+  return ok();
+}
+
+int32_t g4attn_key_range(const g4attn_stack* st, int32_t layer, int64_t q_pos, int64_t n_keys,
+                         int64_t* lo, int64_t* hi) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  if (!lo || !hi) return fail(G4ATTN_ERR_NULL, "lo and hi must be non-NULL");
+  const int W = st->L[layer].d.window;
+  int64_t h = q_pos + 1 < n_keys ? q_pos + 1 : n_keys;
+  if (h < 0) h = 0;
+  int64_t l = 0;
+  if (W > 0) {
+    l = q_pos - W + 1;
+    if (l < 0) l = 0;
+  }
+  if (l > h) l = h;
+  *lo = l;
+  *hi = h;
+  return ok();
+}
+
+int32_t g4attn_kv_offset(const g4attn_stack* st, int32_t layer, int32_t b, int32_t kv_head,
+                         int64_t pos, int32_t d, int64_t* off_k, int64_t* off_v) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  if (!off_k || !off_v) return fail(G4ATTN_ERR_NULL, "off_k and off_v must be non-NULL");
+  const LayerPlan& p = st->L[layer];
+  if (b < 0 || b >= st->max_batch || kv_head < 0 || kv_head >= p.d.n_kv_heads || pos < 0 ||
+      pos >= st->kv_max || d < 0 || d >= p.d.head_dim)
+    return fail(G4ATTN_ERR_RANGE, "(b %d, kv_head %d, pos %lld, d %d) out of range", b, kv_head,
+                (long long)pos, d);
+  const int D = p.d.head_dim;
+  const int64_t slot = pos % p.cap;
+  const int64_t seg = ((int64_t)b * p.d.n_kv_heads + kv_head) * p.cap * D * 2;
+  *off_k = (int64_t)p.k_off + seg + g4::k_elem_offset(slot, d, D);
+  *off_v = p.d.k_eq_v ? *off_k : (int64_t)p.v_off + seg + g4::v_elem_offset(slot, d, D);
+  return ok();
+}
+
+int32_t g4attn_append_kv(const g4attn_stack* st, int32_t layer, const void* k, const void* v,
+                         const int32_t* start_pos, const int32_t* n_valid, int32_t batch,
+                         int32_t n_new, int32_t max_end_pos, void* stream) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  const LayerPlan& p = st->L[layer];
+  if (p.owner != layer)
+    return fail(G4ATTN_ERR_SHARED_LAYER, "layer %d reads layer %d's cache and writes none", layer,
+                p.owner);
+  if (!k || !start_pos) return fail(G4ATTN_ERR_NULL, "k and start_pos must be non-NULL");
+  if (p.d.k_eq_v && v) return fail(G4ATTN_ERR_NULL, "v must be NULL on a k_eq_v layer");
+  if (!p.d.k_eq_v && !v) return fail(G4ATTN_ERR_NULL, "v must be non-NULL");
+  if (batch <= 0 || batch > st->max_batch)
+    return fail(G4ATTN_ERR_RANGE, "batch %d not in [1, %d]", batch, st->max_batch);
+  if (n_new <= 0 || n_new > st->max_chunk)
+    return fail(G4ATTN_ERR_RANGE, "n_new %d not in [1, %d]", n_new, st->max_chunk);
+  if (max_end_pos < 0 || max_end_pos > st->kv_max)
+    return fail(G4ATTN_ERR_RANGE, "max_end_pos %d not in [0, kv_max=%d]", max_end_pos,
+                st->kv_max);
+  if (!st->cache || !st->ws) return fail(G4ATTN_ERR_UNBOUND, "cache/workspace not bound");
+  g4::AppendArgs a;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.kp = reinterpret_cast<uint16_t*>(st->cache + p.k_off);
+  a.vp = p.d.k_eq_v ? nullptr : reinterpret_cast<uint16_t*>(st->cache + p.v_off);
+  a.start = start_pos;
+  a.nvalid = n_valid;
+  a.n_new = n_new;
+  a.n_kv = p.d.n_kv_heads;
+  a.D = p.d.head_dim;
+  a.cap = p.cap;
+  a.kv_max = st->kv_max;
+  hipError_t e = g4::launch_append(a, batch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(G4ATTN_ERR_HIP, "append launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t g4attn_decode(const g4attn_stack* st, int32_t layer, const void* q,
+                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, void* out,
+                      void* stream) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  if (!q || !seq_lens || !out) return fail(G4ATTN_ERR_NULL, "q, seq_lens and out must be non-NULL");
+  if (batch <= 0 || batch > st->max_batch)
+    return fail(G4ATTN_ERR_RANGE, "batch %d not in [1, %d]", batch, st->max_batch);
+  if (max_seq_len < 1 || max_seq_len > st->kv_max)
+    return fail(G4ATTN_ERR_RANGE, "max_seq_len %d not in [1, kv_max=%d]", max_seq_len,
+                st->kv_max);
+  if (!st->cache || !st->ws) return fail(G4ATTN_ERR_UNBOUND, "cache/workspace not bound");
+  const LayerPlan& p = st->L[layer];
+  const g4attn_layer_desc& d = p.d;
+  const int G = d.n_q_heads / d.n_kv_heads;
+  const int n_hblk = (G + 15) / 16;
+  if ((int64_t)d.n_kv_heads * n_hblk > 65535)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "n_kv_heads x head blocks exceeds the launch grid");
+  const int nh = G < 16 ? G : 16;
+  const int keys_max = d.window > 0 && d.window < max_seq_len ? d.window : max_seq_len;
+  g4::DecodeArgs a;
+  const int wgs_per_cu = d.head_dim >= 512 ? 1 : 2;
+  decode_splits(keys_max, batch * d.n_kv_heads * n_hblk, wgs_per_cu, &a.split_keys, &a.n_splits);
+  a.merge_in_kernel =
+      (int64_t)a.n_splits * nh * d.head_dim * 4 <= kInKernelMergeBytes ? 1 : 0;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kp = reinterpret_cast<const uint16_t*>(st->cache + p.k_off);
+  a.vp = reinterpret_cast<const uint16_t*>(st->cache + p.v_off);
+  a.seq_lens = seq_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.counters = reinterpret_cast<int32_t*>(st->ws + st->ws_ctr_off);
+  a.part_ml = reinterpret_cast<float*>(st->ws + st->ws_ml_off);
+  a.part_o = reinterpret_cast<float*>(st->ws + st->ws_o_off);
+  a.n_q = d.n_q_heads;
+  a.n_kv = d.n_kv_heads;
+  a.G = G;
+  a.n_hblk = n_hblk;
+  a.cap = p.cap;
+  a.window = d.window;
+  a.kv_max = st->kv_max;
+  a.scale_log2 = d.scale * 1.4426950408889634f;
+  hipError_t e = g4::launch_decode(d.head_dim, d.k_eq_v != 0, a, batch,
+                                   static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && a.n_splits > 1 && !a.merge_in_kernel) {
+    g4::MergeArgs m{};
+    m.part_o = a.part_o;
+    m.part_ml = a.part_ml;
+    m.out = a.out;
+    m.rows = batch * d.n_q_heads;
+    m.n_splits = a.n_splits;
+    m.D = d.head_dim;
+    m.prefill = 0;
+    e = g4::launch_merge(m, static_cast<hipStream_t>(stream));
+  }
+  if (e != hipSuccess) return fail(G4ATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t g4attn_prefill(const g4attn_stack* st, int32_t layer, const void* q,
+                       const int32_t* start_pos, int32_t batch, int32_t n_tok,
+                       int32_t max_start_pos, void* out, void* stream) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  if (!q || !start_pos || !out)
+    return fail(G4ATTN_ERR_NULL, "q, start_pos and out must be non-NULL");
+  if (batch <= 0 || batch > st->max_batch)
+    return fail(G4ATTN_ERR_RANGE, "batch %d not in [1, %d]", batch, st->max_batch);
+  if (n_tok <= 0 || n_tok > st->max_chunk)
+    return fail(G4ATTN_ERR_RANGE, "n_tok %d not in [1, %d]", n_tok, st->max_chunk);
+  if (max_start_pos < 0 || (int64_t)max_start_pos + n_tok > st->kv_max)
+    return fail(G4ATTN_ERR_RANGE, "max_start_pos %d + n_tok %d exceeds kv_max %d", max_start_pos,
+                n_tok, st->kv_max);
+  if (!st->cache || !st->ws) return fail(G4ATTN_ERR_UNBOUND, "cache/workspace not bound");
+  const LayerPlan& p = st->L[layer];
+  const g4attn_layer_desc& d = p.d;
+  if ((int64_t)batch * d.n_kv_heads > 65535)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "batch x n_kv_heads %lld exceeds the launch grid",
+                (long long)batch * d.n_kv_heads);
+  const int G = d.n_q_heads / d.n_kv_heads;
+  g4::PrefillArgs a;
+  a.rows = n_tok * G;
+  a.n_rowblk = (a.rows + g4::kPrefillRows - 1) / g4::kPrefillRows;
+  const int full = max_start_pos + n_tok;
+  const int span = d.window > 0 && d.window + n_tok - 1 < full ? d.window + n_tok - 1 : full;
+  prefill_splits(span, batch * d.n_kv_heads * a.n_rowblk, g4::prefill_tile(d.head_dim),
+                 g4::kMaxPrefillSplits, &a.split_keys, &a.n_splits);
+  a.merge_in_kernel = (int64_t)a.n_splits * g4::kPrefillRows * d.head_dim * 4 <=
+                              kInKernelMergeBytes ? 1 : 0;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kp = reinterpret_cast<const uint16_t*>(st->cache + p.k_off);
+  a.vp = reinterpret_cast<const uint16_t*>(st->cache + p.v_off);
+  a.start_pos = start_pos;
+  a.out = static_cast<uint16_t*>(out);
+  a.counters = reinterpret_cast<int32_t*>(st->ws + st->ws_ctr_off);
+  a.part_ml = reinterpret_cast<float*>(st->ws + st->ws_ml_off);
+  a.part_o = reinterpret_cast<float*>(st->ws + st->ws_o_off);
+  a.n_q = d.n_q_heads;
+  a.n_kv = d.n_kv_heads;
+  a.G = G;
+  a.T = n_tok;
+  a.cap = p.cap;
+  a.window = d.window;
+  a.kv_max = st->kv_max;
+  a.scale_log2 = d.scale * 1.4426950408889634f;
+  hipError_t e = g4::launch_prefill(d.head_dim, d.k_eq_v != 0, a, batch,
+                                    static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && a.n_splits > 1 && !a.merge_in_kernel) {
+    g4::MergeArgs m{};
+    m.part_o = a.part_o;
+    m.part_ml = a.part_ml;
+    m.out = a.out;
+    m.rows = batch * d.n_kv_heads * a.rows;
+    m.n_splits = a.n_splits;
+    m.D = d.head_dim;
+    m.prefill = 1;
+    m.T = n_tok;
+    m.G = G;
+    m.n_q = d.n_q_heads;
+    m.n_kv = d.n_kv_heads;
+    m.rows_per_group = a.rows;
+    e = g4::launch_merge(m, static_cast<hipStream_t>(stream));
+  }
+  if (e != hipSuccess) return fail(G4ATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
