@@ -66,10 +66,29 @@ struct DecodeArgs {
   float* part_ml;    // [B][n_q][n_splits][2]
   int32_t* counters; // [B][n_kv][n_hblk]
   int n_q, n_kv, G, n_hblk, cap, window, kv_max;
-  int split_keys, n_splits;
+  // A sequence with nb key blocks uses ceil(nb / blocks_per_split) splits
+  // (at most n_splits, the grid's x extent), so every split streams about
+  // the same number of blocks whatever the sequence's length.
+  int blocks_per_split, n_splits;
   int merge_in_kernel;  // 1: last arriving workgroup merges; 0: a merge kernel follows
   float scale_log2;     // scale * log2(e)
 };
+
+// Key blocks [first, end) of split `split` of a sequence whose visible keys
+// are [lo, L), and the number of splits the sequence uses.
+__host__ __device__ inline void decode_split_range(int lo, int L, int KB, int blocks_per_split,
+                                                   int split, int* n_used, int* first,
+                                                   int* end) {
+  const int nb = L > lo ? (L + KB - 1) / KB - lo / KB : 0;
+  const int nu = nb > 0 ? (nb + blocks_per_split - 1) / blocks_per_split : 0;
+  *n_used = nu;
+  if (split >= nu) {
+    *first = *end = 0;
+    return;
+  }
+  *first = lo / KB + (int)(((long long)split * nb) / nu);
+  *end = lo / KB + (int)(((long long)(split + 1) * nb) / nu);
+}
 
 struct PrefillArgs {
   const uint16_t* q;  // [B][T][n_q][D]
@@ -95,6 +114,10 @@ struct MergeArgs {
   // prefill rows are (sequence, KV head, token x head) and land at
   // out[((b * T + t) * n_q + g * G + h) * D]; decode rows at out[row * D]
   int prefill, T, G, n_q, n_kv, rows_per_group;
+  // decode: splits in use per row follow from the sequence's length; rows of
+  // sequences with at most one split were written by the decode kernel
+  const int32_t* seq_lens;
+  int window, kv_max, KB, blocks_per_split;
 };
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s);

@@ -127,23 +127,62 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
 // split merge: out[row] = sum_s w_s O_s / sum_s w_s l_s, w_s = 2^(m_s - max m)
 // ---------------------------------------------------------------------------
 
-// In-kernel version, run by the last workgroup of a group to arrive.
+__device__ __forceinline__ void ld8_coherent_nowait(const float* p, float& a, float& b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  f32x2 v;
+  asm volatile("global_load_dwordx2 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
+  a = v[0];
+  b = v[1];
+}
+
+// In-kernel version, run by the last workgroup of a group to arrive.  All
+// (m, l) pairs are fetched in one batch, then the partial outputs in batches
+// of up to 8 splits per thread, so the merge costs a few memory round trips.
+// `ml` is LDS scratch for n_rows * n_splits * 2 floats.
 template <int D>
 __device__ void merge_rows_coherent(const float* part_o, const float* part_ml, size_t row0_part,
                                     int n_rows, int n_splits, uint16_t* out,
-                                    const size_t* out_row_off, float* wgt /*LDS*/,
-                                    float* inv_l /*LDS*/) {
+                                    const size_t* out_row_off, float* ml /*LDS*/,
+                                    float* inv_l /*LDS*/, int row_stride) {
+  // row r's split s lives at (row0_part + r * row_stride + s); n_splits <= row_stride in use
   const int tid = threadIdx.x;
+  const int n_pairs = n_rows * n_splits;
+  {
+    constexpr int PER = 4;
+    float mv[PER], lv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * (int)blockDim.x;
+      const size_t src = row0_part + (size_t)(idx / n_splits) * row_stride + idx % n_splits;
+      if (idx < n_pairs) ld8_coherent_nowait(part_ml + src * 2, mv[i], lv[i]);
+    }
+    wait_vmem();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * (int)blockDim.x;
+      if (idx < n_pairs) {
+        ml[2 * idx] = mv[i];
+        ml[2 * idx + 1] = lv[i];
+      }
+    }
+    for (int idx = tid + PER * (int)blockDim.x; idx < n_pairs; idx += blockDim.x) {
+      const size_t src = row0_part + (size_t)(idx / n_splits) * row_stride + idx % n_splits;
+      ml[2 * idx] = ld_coherent(part_ml + src * 2);
+      ml[2 * idx + 1] = ld_coherent(part_ml + src * 2 + 1);
+    }
+  }
+  __syncthreads();
+  // weights in place of m: w_s = 2^(m_s - max m) over splits with l_s > 0
   for (int r = tid; r < n_rows; r += blockDim.x) {
-    const float* ml = part_ml + (row0_part + (size_t)r * n_splits) * 2;
+    float* p = ml + 2 * r * n_splits;
     float M = kNegInf;
     for (int s = 0; s < n_splits; ++s)
-      if (ld_coherent(ml + 2 * s + 1) > 0.f) M = fmaxf(M, ld_coherent(ml + 2 * s));
+      if (p[2 * s + 1] > 0.f) M = fmaxf(M, p[2 * s]);
     float lsum = 0.f;
     for (int s = 0; s < n_splits; ++s) {
-      const float l = ld_coherent(ml + 2 * s + 1);
-      const float w = l > 0.f ? fast_exp2(ld_coherent(ml + 2 * s) - M) : 0.f;
-      wgt[r * n_splits + s] = w;
+      const float l = p[2 * s + 1];
+      const float w = l > 0.f ? fast_exp2(p[2 * s] - M) : 0.f;
+      p[2 * s] = w;
       lsum += w * l;
     }
     inv_l[r] = lsum > 0.f ? 1.f / lsum : 0.f;
@@ -154,20 +193,20 @@ __device__ void merge_rows_coherent(const float* part_o, const float* part_ml, s
   for (int idx = tid; idx < n_rows * D4; idx += blockDim.x) {
     const int r = idx / D4;
     const int d = 4 * (idx - r * D4);
-    const float* po = part_o + (row0_part + (size_t)r * n_splits) * D + d;
+    const float* po = part_o + (row0_part + (size_t)r * row_stride) * D + d;
+    const float* wr = ml + 2 * r * n_splits;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < n_splits; s0 += BATCH) {
       f32x4 v[BATCH];
 #pragma unroll
       for (int i = 0; i < BATCH; ++i)
-        if (s0 + i < n_splits && wgt[r * n_splits + s0 + i] != 0.f)
-          v[i] = ld16_coherent_nowait(po + (size_t)(s0 + i) * D);
+        if (s0 + i < n_splits) v[i] = ld16_coherent_nowait(po + (size_t)(s0 + i) * D);
       wait_vmem();
 #pragma unroll
       for (int i = 0; i < BATCH; ++i)
         if (s0 + i < n_splits) {
-          const float w = wgt[r * n_splits + s0 + i];
-          if (w != 0.f) acc += w * v[i];
+          const float w = wr[2 * (s0 + i)];
+          if (w != 0.f) acc += w * v[i];  // empty splits hold stale data: skip them
         }
     }
     const float il = inv_l[r];
@@ -192,26 +231,46 @@ __global__ __launch_bounds__(128) void merge_kernel(MergeArgs a) {
     const int t = r / a.G, h = r - (r / a.G) * a.G;
     out_off = (((size_t)b * a.T + t) * a.n_q + g * a.G + h) * a.D;
   }
+  int n_used = a.n_splits;
+  if (!a.prefill) {
+    const int bseq = (int)(row / a.n_q);
+    int L = a.seq_lens[bseq];
+    L = L < 0 ? 0 : (L > a.kv_max ? a.kv_max : L);
+    const int lo = a.window > 0 ? max(0, L - a.window) : 0;
+    int f, e;
+    decode_split_range(lo, L, a.KB, a.blocks_per_split, 0, &n_used, &f, &e);
+    if (n_used <= 1) return;  // written by the decode kernel itself
+  }
   const float* ml = a.part_ml + row * a.n_splits * 2;
-  if (threadIdx.x == 0) {
-    float M = kNegInf;
-    for (int s = 0; s < a.n_splits; ++s)
-      if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
-    float lsum = 0.f;
-    for (int s = 0; s < a.n_splits; ++s) {
-      const float l = ml[2 * s + 1];
-      const float w = l > 0.f ? fast_exp2(ml[2 * s] - M) : 0.f;
-      wgt[s] = w;
-      lsum += w * l;
-    }
-    s_inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  // every thread of the first wave takes one split; a wave-wide max/sum
+  if (threadIdx.x < 64) {
+    const int s = threadIdx.x;
+    const bool ok = s < n_used;
+    const float m = ok ? ml[2 * s] : kNegInf;
+    const float l = ok ? ml[2 * s + 1] : 0.f;
+    float M = l > 0.f ? m : kNegInf;
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float w = l > 0.f ? fast_exp2(m - M) : 0.f;
+    float lsum = w * l;
+    for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
+    if (ok) wgt[s] = w;
+    if (s == 0) s_inv = lsum > 0.f ? 1.f / lsum : 0.f;
   }
   __syncthreads();
   const float* po = a.part_o + row * a.n_splits * a.D;
+  constexpr int BATCH = 8;
   for (int d = 4 * threadIdx.x; d < a.D; d += 4 * blockDim.x) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.n_splits; ++s)
-      if (wgt[s] != 0.f) acc += wgt[s] * *reinterpret_cast<const f32x4*>(po + (size_t)s * a.D + d);
+    for (int s0 = 0; s0 < n_used; s0 += BATCH) {
+      f32x4 v[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i)
+        if (s0 + i < n_used)
+          v[i] = *reinterpret_cast<const f32x4*>(po + (size_t)(s0 + i) * a.D + d);
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i)
+        if (s0 + i < n_used && wgt[s0 + i] != 0.f) acc += wgt[s0 + i] * v[i];
+    }
     bf16x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = (__bf16)(acc[j] * s_inv);
@@ -240,7 +299,7 @@ struct DecodeShape {
   static constexpr int NDB = D / 16;         // 16-dim output blocks
   static constexpr int RED_FLOATS = 16 * D;  // cross-wave reduction buffer
   static constexpr int TR_ELEMS = KEQV ? 16 * D : 0;  // per-wave transpose area
-  static constexpr int MERGE_BYTES = (16 * kMaxDecodeSplits + 16) * 4;
+  static constexpr int MERGE_BYTES = (2 * 16 * kMaxDecodeSplits + 16) * 4;
   static constexpr int A_BYTES = (4 * TR_ELEMS * 2 > RED_FLOATS * 4) ? 4 * TR_ELEMS * 2 : RED_FLOATS * 4;
   static constexpr int LDS_BYTES = A_BYTES > MERGE_BYTES ? A_BYTES : MERGE_BYTES;
 };
@@ -270,23 +329,56 @@ __global__ __launch_bounds__(256, D >= 512 ? 1 : 2) void decode_kernel(DecodeArg
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > a.kv_max ? a.kv_max : L);
   const int lo = a.window > 0 ? max(0, L - a.window) : 0;
-  const int base = lo & ~63;  // splits are aligned to 64 positions
-  const int r_beg = max(lo, base + split * a.split_keys);
-  const int r_end = min(L, base + (split + 1) * a.split_keys);
+  // the sequence's KB-aligned blocks are dealt out evenly to the splits it
+  // uses; the number it uses grows with its length
+  int n_used, blk_first, blk_end;
+  decode_split_range(lo, L, KB, a.blocks_per_split, split, &n_used, &blk_first, &blk_end);
+  if (split > 0 && split >= n_used) return;  // nothing for this workgroup
+  const bool direct = n_used <= 1;           // write the output, no partials
+  const int r_beg = max(lo, blk_first * KB);
+  const int r_end = min(L, blk_end * KB);
   const int n_keys = r_end - r_beg;
 
   const size_t seg = (size_t)(b * a.n_kv + g) * a.cap * D;
   const uint16_t* kseg = a.kp + seg;
   const uint16_t* vseg = a.vp + seg;
 
-  // queries as the B operand of S^T = K Q^T: column c16 = head, k-slots = dims
-  bf16x8 qf[KS];
+  // loads of a wave's next block are issued as soon as the registers they
+  // land in are free (K after the scores, V after the PV product), so they
+  // overlap the rest of the current block
+  u32x4 kreg[NSB][KS];
+  u32x4 vreg[KEQV ? 1 : NDB];
+  auto load_k = [&](int blk) {
+    const int slot0 = (blk * KB) % a.cap;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        kreg[sb][s] = ldg16(kseg + ((size_t)(slot0 / 16 + sb) * KS + s) * 512 + lane * 8);
+  };
+  auto load_v = [&](int blk) {
+    if constexpr (!KEQV) {
+      const int slot0 = (blk * KB) % a.cap;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        vreg[db] = ldg16(vseg + ((size_t)(slot0 / 32) * NDB + db) * 512 + lane * 8);
+    }
+  };
+  if (n_keys > 0 && blk_first + w < blk_end) {
+    load_k(blk_first + w);
+    load_v(blk_first + w);
+  }
+
+  // queries as the B operand of S^T = K Q^T (column c16 = head, k-slots =
+  // dims), kept in LDS in operand order: sub-tile s, lane L at (s*64 + L)*8
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[KS * 512];
   {
     const uint16_t* qrow = a.q + ((size_t)b * a.n_q + head0 + c16) * D + 8 * q4;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qf[s] = c16 < nh ? as_bf16x8(ldg16(qrow + 32 * s)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    for (int s = w; s < KS; s += 4)
+      *reinterpret_cast<u32x4*>(&Qs[(s * 64 + lane) * 8]) =
+          c16 < nh ? ldg16(qrow + 32 * s) : u32x4{0u, 0u, 0u, 0u};
   }
+  __syncthreads();
 
   f32x4 oacc[NDB];
 #pragma unroll
@@ -297,33 +389,36 @@ __global__ __launch_bounds__(256, D >= 512 ? 1 : 2) void decode_kernel(DecodeArg
   uint16_t* tr = reinterpret_cast<uint16_t*>(lds) + w * S::TR_ELEMS;  // k_eq_v only
 
   if (n_keys > 0) {
-    const int blk_first = r_beg / KB;
-    const int blk_end = (r_end + KB - 1) / KB;
     for (int blk = blk_first + w; blk < blk_end; blk += 4) {
       const int pos0 = blk * KB;
-      const int slot0 = pos0 % a.cap;
-      u32x4 kreg[NSB][KS];
-#pragma unroll
-      for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          kreg[sb][s] = ldg16(kseg + ((size_t)(slot0 / 16 + sb) * KS + s) * 512 + lane * 8);
-      u32x4 vreg[KEQV ? 1 : NDB];
-      if constexpr (!KEQV) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          vreg[db] = ldg16(vseg + ((size_t)(slot0 / 32) * NDB + db) * 512 + lane * 8);
-      }
+      const bool has_next = blk + 4 < blk_end;
       const bool full = pos0 >= r_beg && pos0 + KB <= r_end;
 
-      // scores, mask, online softmax (lane's column c16 = head)
+      // scores, mask, online softmax (lane's column c16 = head).  The compiler
+      // barrier keeps the query reads from LDS here instead of hoisting the
+      // whole query operand into registers for the loop.
+      asm volatile("" ::: "memory");
       f32x4 sacc[NSB];
-      float lmax = kNegInf;
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) {
         sacc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) sacc[sb] = mfma32(as_bf16x8(kreg[sb][s]), qf[s], sacc[sb]);
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 qf = *reinterpret_cast<const bf16x8*>(&Qs[(s * 64 + lane) * 8]);
+          sacc[sb] = mfma32(as_bf16x8(kreg[sb][s]), qf, sacc[sb]);
+        }
+      }
+      if constexpr (KEQV) {
+        // the K block doubles as V: stage it in this wave's LDS area in its
+        // operand order, to be read back transposed
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[0][s];
+      }
+      if (has_next) load_k(blk + 4);
+      float lmax = kNegInf;
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int kpos = pos0 + 16 * sb + 4 * q4 + j;
@@ -373,12 +468,8 @@ __global__ __launch_bounds__(256, D >= 512 ? 1 : 2) void decode_kernel(DecodeArg
           }
           oacc[db] = mfma32(vf, pf, oacc[db]);
         }
+        if (has_next) load_v(blk + 4);
       } else {
-        // the K block doubles as V: stage it in this wave's LDS area in its
-        // operand order and read V^T back with 16-bit loads
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[0][s];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int d = 16 * db + c16;
@@ -435,7 +526,7 @@ __global__ __launch_bounds__(256, D >= 512 ? 1 : 2) void decode_kernel(DecodeArg
   }
 
   // red[h][:] = unnormalised O of this key range for head h; hM, hL per head
-  if (a.n_splits == 1) {
+  if (direct) {
     for (int idx = tid; idx < nh * D4; idx += 256) {
       const int h = idx / D4;
       const int d = 4 * (idx - h * D4);
@@ -475,15 +566,15 @@ __global__ __launch_bounds__(256, D >= 512 ? 1 : 2) void decode_kernel(DecodeArg
   if (!a.merge_in_kernel) return;
   wait_vmem();
   int32_t* ctr = a.counters + ((size_t)b * a.n_kv + g) * a.n_hblk + hblk;
-  if (!arrive_last(ctr, a.n_splits, &s_flag)) return;
+  if (!arrive_last(ctr, n_used, &s_flag)) return;
 
-  float* wgt = reinterpret_cast<float*>(lds);  // 16 x n_splits floats
-  float* inv_l = wgt + 16 * kMaxDecodeSplits;
+  float* wgt = reinterpret_cast<float*>(lds);  // 16 x n_splits (m, l) pairs
+  float* inv_l = wgt + 2 * 16 * kMaxDecodeSplits;
   __shared__ size_t out_off[16];
   if (tid < nh) out_off[tid] = ((size_t)b * a.n_q + head0 + tid) * D;
   __syncthreads();
   merge_rows_coherent<D>(a.part_o, a.part_ml, ((size_t)b * a.n_q + head0) * a.n_splits, nh,
-                         a.n_splits, a.out, out_off, wgt, inv_l);
+                         n_used, a.out, out_off, wgt, inv_l, a.n_splits);
   if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -507,7 +598,9 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   constexpr int CH_TILE = K_ELEMS / 8;      // 16-byte chunks per plane tile
   constexpr int CH_THR = (CH_TILE + 255) / 256;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[K_ELEMS];
+  // the K tile's space also serves the split merge: (m, l) per row and split
+  constexpr int MERGE_ELEMS = 2 * (2 * kPrefillRows * kMaxPrefillSplits + kPrefillRows);
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[K_ELEMS > MERGE_ELEMS ? K_ELEMS : MERGE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[KEQV ? 8 : V_ELEMS];
   __shared__ int s_flag;
 
@@ -732,8 +825,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   if (!arrive_last(ctr, a.n_splits, &s_flag)) return;
 
   const int n_rows = last_row - rowbase + 1;
-  float* wgt = reinterpret_cast<float*>(Ks);  // kPrefillRows x n_splits
-  float* inv_l = wgt + kPrefillRows * kMaxPrefillSplits;
+  float* wgt = reinterpret_cast<float*>(Ks);  // kPrefillRows x n_splits (m, l) pairs
+  float* inv_l = wgt + 2 * kPrefillRows * kMaxPrefillSplits;
   __shared__ size_t out_off[kPrefillRows];
   if (tid < n_rows) {
     const int r = rowbase + tid;
@@ -743,7 +836,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   }
   __syncthreads();
   merge_rows_coherent<D>(a.part_o, a.part_ml, (grp_row0 + rowbase) * a.n_splits, n_rows,
-                         a.n_splits, a.out, out_off, wgt, inv_l);
+                         a.n_splits, a.out, out_off, wgt, inv_l, a.n_splits);
   if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

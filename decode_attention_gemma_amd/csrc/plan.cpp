@@ -81,19 +81,20 @@ int32_t check_layer(const g4attn_stack* st, int32_t layer) {
   return G4ATTN_OK;
 }
 
-// Decode split policy: enough workgroups to keep every CU busy with a few
-// independent waves, splits aligned to 64 positions.
-void decode_splits(int keys_max, int pairs, int wgs_per_cu, int* split_keys, int* n_splits) {
-  const int span = keys_max + 63;  // alignment slack of the first split
+// Decode split policy: splits hold a fixed number of key blocks, sized so
+// that a sequence of the longest (hinted) length uses enough splits for the
+// grid to cover every CU `wgs_per_cu` times; shorter sequences use fewer.
+void decode_splits(int keys_max, int KB, int pairs, int wgs_per_cu, int* blocks_per_split,
+                   int* n_splits) {
+  const int nb_max = (keys_max + KB - 1) / KB + 1;  // +1: alignment of the first block
   const int target_wgs = 256 * wgs_per_cu;
   int ns = ceil_div(target_wgs, pairs);
   if (ns > g4::kMaxDecodeSplits) ns = g4::kMaxDecodeSplits;
+  if (ns > nb_max) ns = nb_max;
   if (ns < 1) ns = 1;
-  int sk = ceil_div(ceil_div(span, ns), 64) * 64;
-  if (sk < 64) sk = 64;
-  *split_keys = sk;
-  *n_splits = ceil_div(span, sk);
-  if (*n_splits < 1) *n_splits = 1;
+  int bps = ceil_div(nb_max, ns);
+  *blocks_per_split = bps;
+  *n_splits = ceil_div(nb_max, bps);
 }
 
 void prefill_splits(int span, int pairs, int KT, int max_splits, int* split_keys,
@@ -370,7 +371,9 @@ int32_t g4attn_decode(const g4attn_stack* st, int32_t layer, const void* q,
   const int keys_max = d.window > 0 && d.window < max_seq_len ? d.window : max_seq_len;
   g4::DecodeArgs a;
   const int wgs_per_cu = d.head_dim >= 512 ? 1 : 2;
-  decode_splits(keys_max, batch * d.n_kv_heads * n_hblk, wgs_per_cu, &a.split_keys, &a.n_splits);
+  const int KB = g4::decode_block(d.k_eq_v != 0);
+  decode_splits(keys_max, KB, batch * d.n_kv_heads * n_hblk, wgs_per_cu, &a.blocks_per_split,
+                &a.n_splits);
   a.merge_in_kernel =
       (int64_t)a.n_splits * nh * d.head_dim * 4 <= kInKernelMergeBytes ? 1 : 0;
   a.q = static_cast<const uint16_t*>(q);
@@ -400,6 +403,12 @@ int32_t g4attn_decode(const g4attn_stack* st, int32_t layer, const void* q,
     m.n_splits = a.n_splits;
     m.D = d.head_dim;
     m.prefill = 0;
+    m.n_q = d.n_q_heads;
+    m.seq_lens = seq_lens;
+    m.window = d.window;
+    m.kv_max = st->kv_max;
+    m.KB = KB;
+    m.blocks_per_split = a.blocks_per_split;
     e = g4::launch_merge(m, static_cast<hipStream_t>(stream));
   }
   if (e != hipSuccess) return fail(G4ATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
