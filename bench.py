@@ -212,6 +212,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run one 1 GiB device copy, the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention path here runs on a single "
@@ -228,6 +230,15 @@ def main():
         sys.exit(1)
     g4attn.load()
     stream = torch.cuda.Stream()
+    if args.copy_calib:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 1 GiB device-to-device copy done")
+        del src, dst
+        torch.cuda.empty_cache()
     dec = bench_decode(args, stream)
     prefill = {}
     if not args.no_prefill:

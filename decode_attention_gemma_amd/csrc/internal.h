@@ -25,13 +25,10 @@ namespace g4 {
 
 // Upper bound on decode key splits per (sequence, head block).
 constexpr int kMaxDecodeSplits = 64;
-// Upper bound on prefill key splits per (sequence, KV head, row block).
-constexpr int kMaxPrefillSplits = 8;
 // Query rows (token x head pairs) per prefill workgroup.
-constexpr int kPrefillRows = 64;
+constexpr int kPrefillRows = 16;
 
 inline int decode_block(bool k_eq_v) { return k_eq_v ? 16 : 32; }
-inline int prefill_tile(int head_dim) { return head_dim >= 512 ? 32 : 64; }
 
 // Byte offsets of element d of the K row / V row in one segment.
 __host__ __device__ inline int64_t k_elem_offset(int64_t slot, int d, int D) {
@@ -95,26 +92,20 @@ struct PrefillArgs {
   const uint16_t* kp;
   const uint16_t* vp;  // == kp when k_eq_v
   const int32_t* start_pos;
-  uint16_t* out;      // [B][T][n_q][D]
-  float* part_o;      // [B][n_kv][T*G][n_splits][D]
-  float* part_ml;     // [B][n_kv][T*G][n_splits][2]
-  int32_t* counters;  // [B][n_kv][n_rowblk]
-  int n_q, n_kv, G, T, cap, window, kv_max;
+  uint16_t* out;  // [B][T][n_q][D]
+  int batch, n_q, n_kv, G, T, cap, window, kv_max;
+  // rows = T * G (token-major (token, head) pairs of one KV head), in
+  // n_rowblk blocks of kPrefillRows
   int rows, n_rowblk;
-  int split_keys, n_splits;
-  int merge_in_kernel;
   float scale_log2;
 };
 
 struct MergeArgs {
-  const float* part_o;   // [rows][n_splits][D]
+  const float* part_o;   // [rows][n_splits][D], rows = (sequence, query head)
   const float* part_ml;  // [rows][n_splits][2]
-  uint16_t* out;
-  int rows, n_splits, D;
-  // prefill rows are (sequence, KV head, token x head) and land at
-  // out[((b * T + t) * n_q + g * G + h) * D]; decode rows at out[row * D]
-  int prefill, T, G, n_q, n_kv, rows_per_group;
-  // decode: splits in use per row follow from the sequence's length; rows of
+  uint16_t* out;         // row r at out[r * D]
+  int rows, n_splits, D, n_q;
+  // splits in use per row follow from the sequence's length; rows of
   // sequences with at most one split were written by the decode kernel
   const int32_t* seq_lens;
   int window, kv_max, KB, blocks_per_split;
@@ -122,8 +113,7 @@ struct MergeArgs {
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s);
 hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, int batch, hipStream_t s);
-hipError_t launch_prefill(int head_dim, bool k_eq_v, const PrefillArgs& a, int batch,
-                          hipStream_t s);
+hipError_t launch_prefill(int head_dim, bool k_eq_v, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 
 }  // namespace g4

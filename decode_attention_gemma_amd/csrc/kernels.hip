@@ -217,101 +217,144 @@ __device__ void merge_rows_coherent(const float* part_o, const float* part_ml, s
   }
 }
 
-// Stand-alone version: one workgroup per output row; partials are ordinary
-// global memory here (a kernel boundary separates writer and reader).
-__global__ __launch_bounds__(128) void merge_kernel(MergeArgs a) {
-  __shared__ float wgt[kMaxDecodeSplits];
-  __shared__ float s_inv;
-  const size_t row = blockIdx.x;
-  size_t out_off = row * a.D;
-  if (a.prefill) {
-    const int grp = (int)(row / a.rows_per_group);
-    const int r = (int)(row - (size_t)grp * a.rows_per_group);
-    const int b = grp / a.n_kv, g = grp - (grp / a.n_kv) * a.n_kv;
-    const int t = r / a.G, h = r - (r / a.G) * a.G;
-    out_off = (((size_t)b * a.T + t) * a.n_q + g * a.G + h) * a.D;
-  }
-  int n_used = a.n_splits;
-  if (!a.prefill) {
-    const int bseq = (int)(row / a.n_q);
-    int L = a.seq_lens[bseq];
-    L = L < 0 ? 0 : (L > a.kv_max ? a.kv_max : L);
-    const int lo = a.window > 0 ? max(0, L - a.window) : 0;
-    int f, e;
-    decode_split_range(lo, L, a.KB, a.blocks_per_split, 0, &n_used, &f, &e);
-    if (n_used <= 1) return;  // written by the decode kernel itself
-  }
-  const float* ml = a.part_ml + row * a.n_splits * 2;
-  // every thread of the first wave takes one split; a wave-wide max/sum
-  if (threadIdx.x < 64) {
-    const int s = threadIdx.x;
-    const bool ok = s < n_used;
-    const float m = ok ? ml[2 * s] : kNegInf;
-    const float l = ok ? ml[2 * s + 1] : 0.f;
-    float M = l > 0.f ? m : kNegInf;
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float w = l > 0.f ? fast_exp2(m - M) : 0.f;
-    float lsum = w * l;
-    for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
-    if (ok) wgt[s] = w;
-    if (s == 0) s_inv = lsum > 0.f ? 1.f / lsum : 0.f;
+// Stand-alone version for large decode merges (a kernel boundary separates
+// writer and reader, so ordinary loads see the partials).  A workgroup takes
+// R = max(64, D/4) / (D/4) rows; every thread owns one 4-dim slice of a row
+// and issues the loads of all of that row's splits at once, so the merge
+// costs two memory round trips.
+template <int D>
+__global__ __launch_bounds__(D / 4 > 64 ? D / 4 : 64) void merge_kernel(MergeArgs a) {
+  constexpr int D4 = D / 4;
+  constexpr int NT = D4 > 64 ? D4 : 64;
+  constexpr int R = NT / D4;
+  constexpr int CH = 16;  // splits loaded per batch
+  __shared__ float wgt[R][kMaxDecodeSplits];
+  __shared__ float lval[R][kMaxDecodeSplits];
+  __shared__ float s_inv[R];
+  __shared__ int s_used[R];
+  const int tid = threadIdx.x;
+  const size_t row0 = (size_t)blockIdx.x * R;
+
+  // splits in use and output offset of each row of this workgroup
+  if (tid < R) {
+    const size_t row = row0 + tid;
+    int n_used = 0;
+    if (row < (size_t)a.rows) {
+      const int bseq = (int)(row / a.n_q);
+      int L = a.seq_lens[bseq];
+      L = L < 0 ? 0 : (L > a.kv_max ? a.kv_max : L);
+      const int lo = a.window > 0 ? max(0, L - a.window) : 0;
+      int f, e;
+      decode_split_range(lo, L, a.KB, a.blocks_per_split, 0, &n_used, &f, &e);
+      if (n_used <= 1) n_used = 0;  // written by the decode kernel itself
+    }
+    s_used[tid] = n_used;
   }
   __syncthreads();
-  const float* po = a.part_o + row * a.n_splits * a.D;
-  constexpr int BATCH = 8;
-  for (int d = 4 * threadIdx.x; d < a.D; d += 4 * blockDim.x) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < n_used; s0 += BATCH) {
-      f32x4 v[BATCH];
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i)
-        if (s0 + i < n_used)
-          v[i] = *reinterpret_cast<const f32x4*>(po + (size_t)(s0 + i) * a.D + d);
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i)
-        if (s0 + i < n_used && wgt[s0 + i] != 0.f) acc += wgt[s0 + i] * v[i];
+  // (m, l) pairs: one per thread, all rows of the workgroup at once
+  for (int i = tid; i < R * a.n_splits; i += NT) {
+    const int r = i / a.n_splits, s = i - (i / a.n_splits) * a.n_splits;
+    if (s < s_used[r]) {
+      const float* ml = a.part_ml + ((row0 + r) * a.n_splits + s) * 2;
+      wgt[r][s] = ml[0];
+      lval[r][s] = ml[1];
     }
+  }
+  __syncthreads();
+  if (tid < R && s_used[tid] > 0) {
+    const int n = s_used[tid];
+    float M = kNegInf;
+    for (int s = 0; s < n; ++s)
+      if (lval[tid][s] > 0.f) M = fmaxf(M, wgt[tid][s]);
+    float lsum = 0.f;
+    for (int s = 0; s < n; ++s) {
+      const float l = lval[tid][s];
+      const float w = l > 0.f ? fast_exp2(wgt[tid][s] - M) : 0.f;
+      wgt[tid][s] = w;
+      lsum += w * l;
+    }
+    s_inv[tid] = lsum > 0.f ? 1.f / lsum : 0.f;
+  }
+  __syncthreads();
+
+  for (int item = tid; item < R * D4; item += NT) {
+    const int r = item / D4;
+    const int d = 4 * (item - r * D4);
+    const int n = s_used[r];
+    const size_t row = row0 + r;
+    if (n == 0 || row >= (size_t)a.rows) continue;
+    const float* po = a.part_o + row * a.n_splits * D + d;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < n; s0 += CH) {
+      f32x4 v[CH];
+#pragma unroll
+      for (int i = 0; i < CH; ++i)
+        if (s0 + i < n) v[i] = *reinterpret_cast<const f32x4*>(po + (size_t)(s0 + i) * D);
+#pragma unroll
+      for (int i = 0; i < CH; ++i)
+        if (s0 + i < n && wgt[r][s0 + i] != 0.f) acc += wgt[r][s0 + i] * v[i];
+    }
+    const size_t out_off = row * D;
     bf16x4 o;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = (__bf16)(acc[j] * s_inv);
+    for (int j = 0; j < 4; ++j) o[j] = (__bf16)(acc[j] * s_inv[r]);
     *reinterpret_cast<bf16x4*>(a.out + out_off + d) = o;
   }
 }
 
 // ---------------------------------------------------------------------------
-// decode: one workgroup per (key split, KV head x head block, sequence)
+// attention over cached key blocks: decode and prefill share one kernel body
 // ---------------------------------------------------------------------------
 //
-// The workgroup's key range is cut into blocks of KB keys (32, or 16 on k_eq_v
-// layers), and wave w takes blocks w, w+4, ...: each wave streams its blocks
-// straight from HBM into registers in operand order (1 KiB contiguous per load
-// instruction), keeps its own online-softmax state, and needs no barrier until
-// the four waves combine their states through LDS at the end.  Latency is
-// hidden by occupancy (several independent waves per SIMD) rather than by a
-// shared pipeline.  On k_eq_v layers the K block is the V block as well; it is
-// written once to a wave-private LDS area and read back transposed.
+// A workgroup owns up to 16 query rows and a range of key blocks (KB keys:
+// 32, or 16 on k_eq_v layers).  Wave w of NW takes blocks w, w+NW, ...: it
+// streams each block straight from the cache into registers in operand order
+// (1 KiB contiguous per load instruction), computes S^T = K Q^T on MFMA with
+// the queries read from LDS, keeps its own online-softmax state per row, and
+// accumulates O^T = V^T P^T.  On k_eq_v layers the K block is the V block as
+// well: it is staged in a wave-private LDS area and read back transposed with
+// ds_read_b64_tr_b16.  No barrier is needed until the NW waves combine their
+// states through LDS at the end; latency is hidden by occupancy.
+//
+// Decode (one query position per sequence): the rows are the query heads of
+// one KV head; the sequence's blocks are split over workgroups in proportion
+// to its length and the splits are merged (in-kernel or by merge_kernel).
+// Prefill (a chunk of T tokens): the rows are 16 consecutive (token, head)
+// pairs of one KV head, each with its own causal / sliding window; one
+// workgroup streams the whole key range its rows can see, so no split
+// results exist.  The grid is laid out so that the row blocks of one
+// (sequence, KV head) run on the same XCD and share its L2.
 
-template <int D, bool KEQV>
-struct DecodeShape {
+template <int D, bool KEQV, int NW>
+struct Shape {
   static constexpr int KB = KEQV ? 16 : 32;  // keys per block
   static constexpr int NSB = KB / 16;        // 16-key score blocks per block
   static constexpr int KS = D / 32;          // 1 KiB K sub-tiles per 16 keys
   static constexpr int NDB = D / 16;         // 16-dim output blocks
-  static constexpr int RED_FLOATS = 16 * D;  // cross-wave reduction buffer
-  static constexpr int TR_ELEMS = KEQV ? 16 * D : 0;  // per-wave transpose area
+  // k_eq_v: the block is transposed through LDS in NPH phases of TRH sub-tiles
+  static constexpr int TRH = KS >= 2 ? KS / 2 : KS;
+  static constexpr int NPH = KS / TRH;
+  static constexpr int TR_ELEMS = KEQV ? TRH * 512 : 0;  // per-wave transpose area
+  static constexpr int RED_BYTES = 16 * D * 4;            // cross-wave reduction
   static constexpr int MERGE_BYTES = (2 * 16 * kMaxDecodeSplits + 16) * 4;
-  static constexpr int A_BYTES = (4 * TR_ELEMS * 2 > RED_FLOATS * 4) ? 4 * TR_ELEMS * 2 : RED_FLOATS * 4;
+  static constexpr int TR_BYTES = NW * TR_ELEMS * 2;
+  static constexpr int A_BYTES = TR_BYTES > RED_BYTES ? TR_BYTES : RED_BYTES;
   static constexpr int LDS_BYTES = A_BYTES > MERGE_BYTES ? A_BYTES : MERGE_BYTES;
 };
 
-template <int D, bool KEQV>
-__global__ __launch_bounds__(256, D >= 512 ? 1 : 2) void decode_kernel(DecodeArgs a) {
-  using S = DecodeShape<D, KEQV>;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int D, bool KEQV, int NW, bool PREFILL>
+__global__ __launch_bounds__(NW * 64, (D >= 512 && !KEQV) ? 1 : 2) void attend_kernel(
+    DecodeArgs da, PrefillArgs pa) {
+  using S = Shape<D, KEQV, NW>;
   constexpr int KB = S::KB, NSB = S::NSB, KS = S::KS, NDB = S::NDB;
   constexpr int D4 = D / 4;
+  constexpr int NT = NW * 64;
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::LDS_BYTES];
-  __shared__ float wm[4][16], wl[4][16], hM[16], hL[16];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[KS * 512];
+  __shared__ float wm[NW][16], wl[NW][16], hM[16], hL[16];
   __shared__ int s_flag;
 
   const int tid = threadIdx.x;
@@ -319,37 +362,95 @@ __global__ __launch_bounds__(256, D >= 512 ? 1 : 2) void decode_kernel(DecodeArg
   const int w = tid >> 6;
   const int c16 = lane & 15;
   const int q4 = lane >> 4;
-  const int split = blockIdx.x;
-  const int g = blockIdx.y / a.n_hblk;
-  const int hblk = blockIdx.y - g * a.n_hblk;
-  const int b = blockIdx.z;
-  const int head0 = g * a.G + hblk * 16;
-  const int nh = min(16, a.G - hblk * 16);
 
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.kv_max ? a.kv_max : L);
-  const int lo = a.window > 0 ? max(0, L - a.window) : 0;
-  // the sequence's KB-aligned blocks are dealt out evenly to the splits it
-  // uses; the number it uses grows with its length
-  int n_used, blk_first, blk_end;
-  decode_split_range(lo, L, KB, a.blocks_per_split, split, &n_used, &blk_first, &blk_end);
-  if (split > 0 && split >= n_used) return;  // nothing for this workgroup
-  const bool direct = n_used <= 1;           // write the output, no partials
-  const int r_beg = max(lo, blk_first * KB);
-  const int r_end = min(L, blk_end * KB);
+  // ---- work of this workgroup -------------------------------------------
+  int b, g, cap, n_kv;
+  int blk_first, blk_end;   // key blocks it streams
+  int r_beg, r_end;         // keys it may read; values outside are zeroed
+  int full_lo, full_hi;     // keys visible to every valid row
+  int row_lo, row_hi;       // keys visible to this lane's row (column c16)
+  int nrows;                // valid rows (heads / token-head pairs)
+  bool row_ok;
+  const uint16_t* qrow;     // this lane's query row
+  float scale_log2;
+  // decode only
+  int split = 0, n_used = 1, head0 = 0, hblk = 0;
+  // prefill only
+  int row0 = 0, t_row = 0, h_row = 0;
+  if constexpr (!PREFILL) {
+    const DecodeArgs& a = da;
+    split = blockIdx.x;
+    g = blockIdx.y / a.n_hblk;
+    hblk = blockIdx.y - g * a.n_hblk;
+    b = blockIdx.z;
+    cap = a.cap;
+    n_kv = a.n_kv;
+    scale_log2 = a.scale_log2;
+    head0 = g * a.G + hblk * 16;
+    nrows = min(16, a.G - hblk * 16);
+    int L = a.seq_lens[b];
+    L = L < 0 ? 0 : (L > a.kv_max ? a.kv_max : L);
+    const int lo = a.window > 0 ? max(0, L - a.window) : 0;
+    decode_split_range(lo, L, KB, a.blocks_per_split, split, &n_used, &blk_first, &blk_end);
+    if (split > 0 && split >= n_used) return;  // nothing for this workgroup
+    r_beg = max(lo, blk_first * KB);
+    r_end = min(L, blk_end * KB);
+    full_lo = r_beg;
+    full_hi = r_end;
+    row_lo = r_beg;
+    row_hi = r_end;
+    row_ok = c16 < nrows;
+    qrow = a.q + ((size_t)b * a.n_q + head0 + c16) * D;
+  } else {
+    const PrefillArgs& a = pa;
+    // physical workgroup p runs on XCD p % 8; give each XCD a contiguous
+    // range of logical (sequence, KV head, row block) work
+    const int n_log = a.n_rowblk * a.n_kv * a.batch;
+    const int per_xcd = (n_log + 7) / 8;  // grid.x == 8 * per_xcd
+    const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (logical >= n_log) return;
+    const int rowblk = logical % a.n_rowblk;
+    const int grp = logical / a.n_rowblk;
+    g = grp % a.n_kv;
+    b = grp / a.n_kv;
+    cap = a.cap;
+    n_kv = a.n_kv;
+    scale_log2 = a.scale_log2;
+    int start = a.start_pos[b];
+    start = start < 0 ? 0 : start;
+    row0 = rowblk * 16;
+    nrows = min(16, a.rows - row0);
+    const int row = row0 + c16;
+    row_ok = c16 < nrows;
+    t_row = row_ok ? row / a.G : 0;
+    h_row = row_ok ? row - t_row * a.G : 0;
+    const int p_first = start + row0 / a.G;
+    const int p_last = start + (row0 + nrows - 1) / a.G;
+    const int p_row = start + t_row;
+    auto lo_of = [&](int p) { return a.window > 0 ? max(0, p - a.window + 1) : 0; };
+    r_beg = lo_of(p_first);
+    r_end = min(p_last + 1, a.kv_max);
+    blk_first = r_beg / KB;
+    blk_end = r_end > r_beg ? (r_end + KB - 1) / KB : blk_first;
+    full_lo = lo_of(p_last);
+    full_hi = min(p_first + 1, r_end);
+    row_lo = row_ok ? max(lo_of(p_row), r_beg) : 0;
+    row_hi = row_ok ? min(p_row + 1, r_end) : 0;
+    qrow = a.q + (((size_t)b * a.T + t_row) * a.n_q + g * a.G + h_row) * D;
+  }
   const int n_keys = r_end - r_beg;
+  const uint16_t* kp = PREFILL ? pa.kp : da.kp;
+  const uint16_t* vp = PREFILL ? pa.vp : da.vp;
+  const size_t seg = (size_t)(b * n_kv + g) * cap * D;
+  const uint16_t* kseg = kp + seg;
+  const uint16_t* vseg = vp + seg;
 
-  const size_t seg = (size_t)(b * a.n_kv + g) * a.cap * D;
-  const uint16_t* kseg = a.kp + seg;
-  const uint16_t* vseg = a.vp + seg;
-
-  // loads of a wave's next block are issued as soon as the registers they
-  // land in are free (K after the scores, V after the PV product), so they
-  // overlap the rest of the current block
+  // ---- block loads: the next block's K is loaded as soon as the registers
+  // it lands in are free, so it overlaps the rest of the current block ----
   u32x4 kreg[NSB][KS];
   u32x4 vreg[KEQV ? 1 : NDB];
   auto load_k = [&](int blk) {
-    const int slot0 = (blk * KB) % a.cap;
+    const int slot0 = (blk * KB) % cap;
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
@@ -358,7 +459,7 @@ __global__ __launch_bounds__(256, D >= 512 ? 1 : 2) void decode_kernel(DecodeArg
   };
   auto load_v = [&](int blk) {
     if constexpr (!KEQV) {
-      const int slot0 = (blk * KB) % a.cap;
+      const int slot0 = (blk * KB) % cap;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
         vreg[db] = ldg16(vseg + ((size_t)(slot0 / 32) * NDB + db) * 512 + lane * 8);
@@ -369,15 +470,11 @@ __global__ __launch_bounds__(256, D >= 512 ? 1 : 2) void decode_kernel(DecodeArg
     load_v(blk_first + w);
   }
 
-  // queries as the B operand of S^T = K Q^T (column c16 = head, k-slots =
+  // queries as the B operand of S^T = K Q^T (column c16 = row, k-slots =
   // dims), kept in LDS in operand order: sub-tile s, lane L at (s*64 + L)*8
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[KS * 512];
-  {
-    const uint16_t* qrow = a.q + ((size_t)b * a.n_q + head0 + c16) * D + 8 * q4;
-    for (int s = w; s < KS; s += 4)
-      *reinterpret_cast<u32x4*>(&Qs[(s * 64 + lane) * 8]) =
-          c16 < nh ? ldg16(qrow + 32 * s) : u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int s = w; s < KS; s += NW)
+    *reinterpret_cast<u32x4*>(&Qs[(s * 64 + lane) * 8]) =
+        row_ok ? ldg16(qrow + 32 * s + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
   f32x4 oacc[NDB];
@@ -385,16 +482,16 @@ __global__ __launch_bounds__(256, D >= 512 ? 1 : 2) void decode_kernel(DecodeArg
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf;
   float l_run = 0.f;
-
   uint16_t* tr = reinterpret_cast<uint16_t*>(lds) + w * S::TR_ELEMS;  // k_eq_v only
 
   if (n_keys > 0) {
-    for (int blk = blk_first + w; blk < blk_end; blk += 4) {
+    for (int blk = blk_first + w; blk < blk_end; blk += NW) {
       const int pos0 = blk * KB;
-      const bool has_next = blk + 4 < blk_end;
-      const bool full = pos0 >= r_beg && pos0 + KB <= r_end;
+      const bool has_next = blk + NW < blk_end;
+      const bool full = pos0 >= full_lo && pos0 + KB <= full_hi;
+      const bool vfull = pos0 >= r_beg && pos0 + KB <= r_end;
 
-      // scores, mask, online softmax (lane's column c16 = head).  The compiler
+      // scores, mask, online softmax (lane's column c16 = row).  The compiler
       // barrier keeps the query reads from LDS here instead of hoisting the
       // whole query operand into registers for the loop.
       asm volatile("" ::: "memory");
@@ -408,22 +505,17 @@ __global__ __launch_bounds__(256, D >= 512 ? 1 : 2) void decode_kernel(DecodeArg
           sacc[sb] = mfma32(as_bf16x8(kreg[sb][s]), qf, sacc[sb]);
         }
       }
-      if constexpr (KEQV) {
-        // the K block doubles as V: stage it in this wave's LDS area in its
-        // operand order, to be read back transposed
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[0][s];
+      if constexpr (!KEQV) {
+        if (has_next) load_k(blk + NW);
       }
-      if (has_next) load_k(blk + 4);
       float lmax = kNegInf;
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int kpos = pos0 + 16 * sb + 4 * q4 + j;
-          const bool ok = full || (kpos >= r_beg && kpos < r_end);
-          sacc[sb][j] = ok ? sacc[sb][j] * a.scale_log2 : kNegInf;
+          const bool ok = full ? row_ok : (kpos >= row_lo && kpos < row_hi);
+          sacc[sb][j] = ok ? sacc[sb][j] * scale_log2 : kNegInf;
           lmax = fmaxf(lmax, sacc[sb][j]);
         }
       }
@@ -458,7 +550,7 @@ __global__ __launch_bounds__(256, D >= 512 ? 1 : 2) void decode_kernel(DecodeArg
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           bf16x8 vf = as_bf16x8(vreg[db]);
-          if (!full) {  // values of keys outside the range must not reach the MFMA
+          if (!vfull) {  // values of keys outside the range must not reach the MFMA
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               const int kk = (j < 4) ? 4 * q4 + j : 16 + 4 * q4 + j - 4;
@@ -468,29 +560,42 @@ __global__ __launch_bounds__(256, D >= 512 ? 1 : 2) void decode_kernel(DecodeArg
           }
           oacc[db] = mfma32(vf, pf, oacc[db]);
         }
-        if (has_next) load_v(blk + 4);
+        if (has_next) load_v(blk + NW);
       } else {
+        // the K block doubles as V: each phase stages TRH of its sub-tiles in
+        // this wave's LDS area in operand order; one transposing 64-bit read
+        // per lane then yields V[4q .. 4q+3][d0 + c] for a 16-dim block (the
+        // lane addresses key 4q + c/4, dims d0 + 4(c%4) .. +3).  LDS
+        // operations of one wave complete in order.
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int d = 16 * db + c16;
-          const uint16_t* col = tr + (d / 32) * 512 + ((d % 32) / 8) * 128 + (d % 8);
-          bf16x4 vf;
+        for (int ph = 0; ph < S::NPH; ++ph) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int kk = 4 * q4 + j;
-            vf[j] = as_bf16(col[kk * 8]);
-            if (!full) {
-              const int kpos = pos0 + kk;
-              if (kpos < r_beg || kpos >= r_end) vf[j] = (__bf16)0.f;
+          for (int s = 0; s < S::TRH; ++s)
+            *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[0][ph * S::TRH + s];
+#pragma unroll
+          for (int dbl = 0; dbl < NDB / S::NPH; ++dbl) {
+            const int dd = 16 * dbl + 4 * (c16 & 3);  // dim within the staged sub-tiles
+            const int kk = 4 * q4 + (c16 >> 2);
+            uint16_t* src = tr + (dd / 32) * 512 + ((dd % 32) / 8) * 128 + kk * 8 + (dd % 8);
+            const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src);
+            bf16x4 vf = __builtin_bit_cast(bf16x4, raw);
+            if (!vfull) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int kpos = pos0 + 4 * q4 + j;
+                if (kpos < r_beg || kpos >= r_end) vf[j] = (__bf16)0.f;
+              }
             }
+            const int db = ph * (NDB / S::NPH) + dbl;
+            oacc[db] = mfma16(vf, pb[0], oacc[db]);
           }
-          oacc[db] = mfma16(vf, pb[0], oacc[db]);
         }
+        if (has_next) load_k(blk + NW);
       }
     }
   }
 
-  // ---- combine the four waves: common max, rescale, sum through LDS ----
+  // ---- combine the NW waves: common max, rescale, sum through LDS ----
   float lt = l_run;
   lt += __shfl_xor(lt, 16);
   lt += __shfl_xor(lt, 32);
@@ -501,357 +606,110 @@ __global__ __launch_bounds__(256, D >= 512 ? 1 : 2) void decode_kernel(DecodeArg
   __syncthreads();  // also: every wave is done with its transpose area
   float M = kNegInf;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) M = fmaxf(M, wm[i][c16]);
+  for (int i = 0; i < NW; ++i) M = fmaxf(M, wm[i][c16]);
   const float M_use = M == kNegInf ? 0.f : M;
   if (tid < 16) {
     float Lh = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Lh += wl[i][tid] * fast_exp2(wm[i][tid] - M_use);
+    for (int i = 0; i < NW; ++i) Lh += wl[i][tid] * fast_exp2(wm[i][tid] - M_use);
     hM[tid] = M;
     hL[tid] = Lh;
   }
   const float mine = fast_exp2(m_run - M_use);
   float* red = reinterpret_cast<float*>(lds);  // [16][D]
-  for (int step = 3; step >= 0; --step) {
-    if (w == step && c16 < nh) {
+  for (int step = NW - 1; step >= 0; --step) {
+    if (w == step && c16 < nrows) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         float* p = red + c16 * D + 16 * db + 4 * q4;
         f32x4 v = oacc[db] * mine;
-        if (step != 3) v += *reinterpret_cast<f32x4*>(p);
+        if (step != NW - 1) v += *reinterpret_cast<f32x4*>(p);
         *reinterpret_cast<f32x4*>(p) = v;
       }
     }
     __syncthreads();
   }
 
-  // red[h][:] = unnormalised O of this key range for head h; hM, hL per head
-  if (direct) {
-    for (int idx = tid; idx < nh * D4; idx += 256) {
-      const int h = idx / D4;
-      const int d = 4 * (idx - h * D4);
-      const float il = hL[h] > 0.f ? 1.f / hL[h] : 0.f;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(red + h * D + d);
+  // red[r][:] = unnormalised O of this key range for row r; hM, hL per row
+  if (PREFILL || n_used <= 1) {
+    for (int idx = tid; idx < nrows * D4; idx += NT) {
+      const int r = idx / D4;
+      const int d = 4 * (idx - r * D4);
+      const float il = hL[r] > 0.f ? 1.f / hL[r] : 0.f;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(red + r * D + d);
       bf16x4 o;
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j] = (__bf16)(v[j] * il);
-      *reinterpret_cast<bf16x4*>(a.out + ((size_t)b * a.n_q + head0 + h) * D + d) = o;
-    }
-    return;
-  }
-
-  // split partial: (m, l, O) in fp32
-  const size_t prow0 = ((size_t)b * a.n_q + head0) * a.n_splits + split;
-  for (int idx = tid; idx < nh * D4; idx += 256) {
-    const int h = idx / D4;
-    const int d = 4 * (idx - h * D4);
-    const f32x4 v = *reinterpret_cast<const f32x4*>(red + h * D + d);
-    float* dst = a.part_o + (prow0 + (size_t)h * a.n_splits) * D + d;
-    if (a.merge_in_kernel)
-      st16_coherent(dst, v);
-    else
-      *reinterpret_cast<f32x4*>(dst) = v;
-  }
-  if (tid < nh) {
-    float* ml = a.part_ml + (prow0 + (size_t)tid * a.n_splits) * 2;
-    const float lval = n_keys > 0 ? hL[tid] : 0.f;
-    if (a.merge_in_kernel) {
-      st_coherent(ml, hM[tid]);
-      st_coherent(ml + 1, lval);
-    } else {
-      ml[0] = hM[tid];
-      ml[1] = lval;
-    }
-  }
-  if (!a.merge_in_kernel) return;
-  wait_vmem();
-  int32_t* ctr = a.counters + ((size_t)b * a.n_kv + g) * a.n_hblk + hblk;
-  if (!arrive_last(ctr, n_used, &s_flag)) return;
-
-  float* wgt = reinterpret_cast<float*>(lds);  // 16 x n_splits (m, l) pairs
-  float* inv_l = wgt + 2 * 16 * kMaxDecodeSplits;
-  __shared__ size_t out_off[16];
-  if (tid < nh) out_off[tid] = ((size_t)b * a.n_q + head0 + tid) * D;
-  __syncthreads();
-  merge_rows_coherent<D>(a.part_o, a.part_ml, ((size_t)b * a.n_q + head0) * a.n_splits, nh,
-                         n_used, a.out, out_off, wgt, inv_l, a.n_splits);
-  if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// ---------------------------------------------------------------------------
-// prefill: one workgroup per (key split, 64-row block, sequence x KV head)
-// ---------------------------------------------------------------------------
-//
-// Rows of a (sequence, KV head) group are the T x G (token, head) pairs,
-// token-major.  Wave w owns 16 rows: it keeps their queries as MFMA operands
-// in registers and their output O^T in accumulators; the four waves share the
-// K/V tiles, copied verbatim (operand-ordered) from the cache into LDS, so
-// every operand read from LDS is a conflict-free 16 bytes per lane.
-
-template <int D, bool KEQV, int KT>
-__global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
-  constexpr int KS = D / 32;
-  constexpr int NDB = D / 16;
-  constexpr int NKB = KT / 16;              // 16-key score blocks per tile
-  constexpr int K_ELEMS = KT * D;           // K tile (operand order)
-  constexpr int V_ELEMS = KEQV ? 0 : KT * D;
-  constexpr int CH_TILE = K_ELEMS / 8;      // 16-byte chunks per plane tile
-  constexpr int CH_THR = (CH_TILE + 255) / 256;
-
-  // the K tile's space also serves the split merge: (m, l) per row and split
-  constexpr int MERGE_ELEMS = 2 * (2 * kPrefillRows * kMaxPrefillSplits + kPrefillRows);
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[K_ELEMS > MERGE_ELEMS ? K_ELEMS : MERGE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[KEQV ? 8 : V_ELEMS];
-  __shared__ int s_flag;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int c16 = lane & 15;
-  const int q4 = lane >> 4;
-  const int split = blockIdx.x;
-  const int rowblk = blockIdx.y;
-  const int b = blockIdx.z / a.n_kv;
-  const int g = blockIdx.z - b * a.n_kv;
-
-  int start = a.start_pos[b];
-  start = start < 0 ? 0 : start;
-  const int rowbase = rowblk * kPrefillRows;
-  const int last_row = min(a.rows, rowbase + kPrefillRows) - 1;
-  const int p_first = start + rowbase / a.G;
-  const int p_last = start + last_row / a.G;
-  const int kbeg = a.window > 0 ? max(0, p_first - a.window + 1) : 0;
-  const int kend = min(p_last + 1, a.kv_max);
-  const int base = kbeg & ~(KT - 1);  // splits and tiles aligned to KT positions
-  const int r_beg = max(kbeg, base + split * a.split_keys);
-  const int r_end = min(kend, base + (split + 1) * a.split_keys);
-  const int n_keys = r_end - r_beg;
-
-  const int row = rowbase + 16 * w + c16;
-  const bool row_ok = row < a.rows;
-  const int t_row = row_ok ? row / a.G : 0;
-  const int h_row = row_ok ? row - t_row * a.G : 0;
-  const int p_row = start + t_row;
-  const int lo_row = a.window > 0 ? max(0, p_row - a.window + 1) : 0;
-  const int wr0 = min(rowbase + 16 * w, a.rows - 1);
-  const int wr1 = min(rowbase + 16 * w + 15, a.rows - 1);
-  const bool wave_has_rows = rowbase + 16 * w < a.rows;
-  const int w_lo = a.window > 0 ? max(0, start + wr0 / a.G - a.window + 1) : 0;
-  const int w_hi = start + wr1 / a.G + 1;
-
-  const size_t seg = (size_t)(b * a.n_kv + g) * a.cap * D;
-  const uint16_t* kseg = a.kp + seg;
-  const uint16_t* vseg = a.vp + seg;
-
-  bf16x8 qf[KS];
-  {
-    const uint16_t* qrow =
-        a.q + (((size_t)b * a.T + t_row) * a.n_q + g * a.G + h_row) * D + 8 * q4;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qf[s] = row_ok ? as_bf16x8(ldg16(qrow + 32 * s)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-  }
-
-  f32x4 oacc[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf;
-  float l_run = 0.f;
-
-  // a tile is KT consecutive positions starting at a multiple of KT; in the
-  // cache it is one contiguous run of K_ELEMS (and V_ELEMS) elements
-  u32x4 kreg[CH_THR];
-  u32x4 vreg[KEQV ? 1 : CH_THR];
-  auto load_tile = [&](int tpos) {
-    const size_t off = (size_t)(tpos % a.cap) * D;
-#pragma unroll
-    for (int i = 0; i < CH_THR; ++i) {
-      const int c = tid + 256 * i;
-      if (c < CH_TILE) {
-        kreg[i] = ldg16(kseg + off + 8 * c);
-        if constexpr (!KEQV) vreg[i] = ldg16(vseg + off + 8 * c);
-      }
-    }
-  };
-
-  const int t_first = n_keys > 0 ? r_beg / KT : 0;
-  const int t_end = n_keys > 0 ? (r_end + KT - 1) / KT : 0;
-  if (t_end > t_first) load_tile(t_first * KT);
-
-  for (int t = t_first; t < t_end; ++t) {
-    const int tpos = t * KT;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < CH_THR; ++i) {
-      const int c = tid + 256 * i;
-      if (c < CH_TILE) {
-        *reinterpret_cast<u32x4*>(&Ks[8 * c]) = kreg[i];
-        if constexpr (!KEQV) *reinterpret_cast<u32x4*>(&Vs[8 * c]) = vreg[i];
-      }
-    }
-    __syncthreads();
-    if (t + 1 < t_end) load_tile(tpos + KT);
-
-    const int vis_lo_t = max(r_beg, tpos);
-    const int vis_hi_t = min(r_end, tpos + KT);
-    if (!wave_has_rows || vis_lo_t >= w_hi || vis_hi_t <= w_lo) continue;
-    const bool tile_full = vis_lo_t == tpos && vis_hi_t == tpos + KT;
-
-    f32x4 sacc[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[(kb * KS + s) * 512 + lane * 8]);
-        sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
-      }
-    }
-    const int vis_lo = max(lo_row, vis_lo_t);
-    const int vis_hi = min(p_row + 1, vis_hi_t);
-    float lmax = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kpos = tpos + 16 * kb + 4 * q4 + j;
-        const bool ok = row_ok && kpos >= vis_lo && kpos < vis_hi;
-        sacc[kb][j] = ok ? sacc[kb][j] * a.scale_log2 : kNegInf;
-        lmax = fmaxf(lmax, sacc[kb][j]);
-      }
-    }
-    lmax = fmaxf(lmax, __shfl_xor(lmax, 16));
-    lmax = fmaxf(lmax, __shfl_xor(lmax, 32));
-    const float m_new = fmaxf(m_run, lmax);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
-    bf16x4 pb[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const __bf16 p = (__bf16)fast_exp2(sacc[kb][j] - m_use);
-        pb[kb][j] = p;
-        psum += (float)p;
-      }
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
-
-#pragma unroll
-    for (int kk = 0; kk < NKB / 2; ++kk) {
-      bf16x8 pf;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pf[j] = pb[2 * kk][j];
-        pf[4 + j] = pb[2 * kk + 1][j];
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        bf16x8 vf;
-        if constexpr (!KEQV) {
-          vf = *reinterpret_cast<const bf16x8*>(&Vs[(kk * NDB + db) * 512 + lane * 8]);
-        } else {
-          // V^T from the operand-ordered K tile: key kslot(q, j), dim d
-          const int d = 16 * db + c16;
-          const uint16_t* col = &Ks[(d / 32) * 512 + ((d % 32) / 8) * 128 + (d % 8)];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            vf[j] = as_bf16(col[((2 * kk) * KS) * 512 + (4 * q4 + j) * 8]);
-            vf[4 + j] = as_bf16(col[((2 * kk + 1) * KS) * 512 + (4 * q4 + j) * 8]);
-          }
-        }
-        if (!tile_full) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int kkey = 32 * kk + ((j < 4) ? 4 * q4 + j : 16 + 4 * q4 + j - 4);
-            const int kpos = tpos + kkey;
-            if (kpos < vis_lo_t || kpos >= vis_hi_t) vf[j] = (__bf16)0.f;
-          }
-        }
-        oacc[db] = mfma32(vf, pf, oacc[db]);
-      }
-    }
-  }
-
-  float lt = l_run;
-  lt += __shfl_xor(lt, 16);
-  lt += __shfl_xor(lt, 32);
-
-  if (a.n_splits == 1) {
-    if (row_ok) {
-      const float il = lt > 0.f ? 1.f / lt : 0.f;
-      uint16_t* orow = a.out + (((size_t)b * a.T + t_row) * a.n_q + g * a.G + h_row) * D;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        bf16x4 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = (__bf16)(oacc[db][j] * il);
-        *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * q4) = o;
-      }
-    }
-    return;
-  }
-
-  const size_t grp_row0 = (size_t)(b * a.n_kv + g) * a.rows;
-  if (row_ok) {
-    const size_t prow = (grp_row0 + row) * a.n_splits + split;
-    if (n_keys > 0) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        float* dst = a.part_o + prow * D + 16 * db + 4 * q4;
-        if (a.merge_in_kernel)
-          st16_coherent(dst, oacc[db]);
-        else
-          *reinterpret_cast<f32x4*>(dst) = oacc[db];
-      }
-    }
-    if (q4 == 0) {
-      if (a.merge_in_kernel) {
-        st_coherent(a.part_ml + prow * 2, m_run);
-        st_coherent(a.part_ml + prow * 2 + 1, n_keys > 0 ? lt : 0.f);
+      size_t off;
+      if constexpr (PREFILL) {
+        const int rr = row0 + r;
+        const int tt = rr / pa.G;
+        off = (((size_t)b * pa.T + tt) * pa.n_q + g * pa.G + (rr - tt * pa.G)) * D;
       } else {
-        a.part_ml[prow * 2] = m_run;
-        a.part_ml[prow * 2 + 1] = n_keys > 0 ? lt : 0.f;
+        off = ((size_t)b * da.n_q + head0 + r) * D;
+      }
+      *reinterpret_cast<bf16x4*>((PREFILL ? pa.out : da.out) + off + d) = o;
+    }
+    return;
+  }
+
+  if constexpr (!PREFILL) {
+    const DecodeArgs& a = da;
+    // split partial: (m, l, O) in fp32
+    const size_t prow0 = ((size_t)b * a.n_q + head0) * a.n_splits + split;
+    for (int idx = tid; idx < nrows * D4; idx += NT) {
+      const int h = idx / D4;
+      const int d = 4 * (idx - h * D4);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(red + h * D + d);
+      float* dst = a.part_o + (prow0 + (size_t)h * a.n_splits) * D + d;
+      if (a.merge_in_kernel)
+        st16_coherent(dst, v);
+      else
+        *reinterpret_cast<f32x4*>(dst) = v;
+    }
+    if (tid < nrows) {
+      float* ml = a.part_ml + (prow0 + (size_t)tid * a.n_splits) * 2;
+      const float lval = n_keys > 0 ? hL[tid] : 0.f;
+      if (a.merge_in_kernel) {
+        st_coherent(ml, hM[tid]);
+        st_coherent(ml + 1, lval);
+      } else {
+        ml[0] = hM[tid];
+        ml[1] = lval;
       }
     }
-  }
-  if (!a.merge_in_kernel) return;
-  wait_vmem();
-  int32_t* ctr = a.counters + ((size_t)b * a.n_kv + g) * a.n_rowblk + rowblk;
-  if (!arrive_last(ctr, a.n_splits, &s_flag)) return;
+    if (!a.merge_in_kernel) return;
+    wait_vmem();
+    int32_t* ctr = a.counters + ((size_t)b * a.n_kv + g) * a.n_hblk + hblk;
+    if (!arrive_last(ctr, n_used, &s_flag)) return;
 
-  const int n_rows = last_row - rowbase + 1;
-  float* wgt = reinterpret_cast<float*>(Ks);  // kPrefillRows x n_splits (m, l) pairs
-  float* inv_l = wgt + 2 * kPrefillRows * kMaxPrefillSplits;
-  __shared__ size_t out_off[kPrefillRows];
-  if (tid < n_rows) {
-    const int r = rowbase + tid;
-    const int tt = r / a.G;
-    const int hh = r - tt * a.G;
-    out_off[tid] = (((size_t)b * a.T + tt) * a.n_q + g * a.G + hh) * D;
+    float* wgt = reinterpret_cast<float*>(lds);  // 16 x n_splits (m, l) pairs
+    float* inv_l = wgt + 2 * 16 * kMaxDecodeSplits;
+    __shared__ size_t out_off[16];
+    if (tid < nrows) out_off[tid] = ((size_t)b * a.n_q + head0 + tid) * D;
+    __syncthreads();
+    merge_rows_coherent<D>(a.part_o, a.part_ml, ((size_t)b * a.n_q + head0) * a.n_splits,
+                           nrows, n_used, a.out, out_off, wgt, inv_l, a.n_splits);
+    if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  merge_rows_coherent<D>(a.part_o, a.part_ml, (grp_row0 + rowbase) * a.n_splits, n_rows,
-                         a.n_splits, a.out, out_off, wgt, inv_l, a.n_splits);
-  if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, bool KEQV>
 hipError_t decode_launch(const DecodeArgs& a, int batch, hipStream_t s) {
   dim3 grid(a.n_splits, a.n_kv * a.n_hblk, batch);
-  hipLaunchKernelGGL((decode_kernel<D, KEQV>), grid, dim3(256), 0, s, a);
+  PrefillArgs none{};
+  hipLaunchKernelGGL((attend_kernel<D, KEQV, 4, false>), grid, dim3(256), 0, s, a, none);
   return hipGetLastError();
 }
 
 template <int D, bool KEQV>
-hipError_t prefill_launch(const PrefillArgs& a, int batch, hipStream_t s) {
-  dim3 grid(a.n_splits, a.n_rowblk, batch * a.n_kv);
-  constexpr int KT = D >= 512 ? 32 : 64;
-  hipLaunchKernelGGL((prefill_kernel<D, KEQV, KT>), grid, dim3(256), 0, s, a);
+hipError_t prefill_launch(const PrefillArgs& a, hipStream_t s) {
+  // eight waves per row block, four where a wave needs all 512 registers
+  constexpr int NW = (D >= 512 && !KEQV) ? 4 : 8;
+  const int n_log = a.n_rowblk * a.n_kv * a.batch;
+  dim3 grid(8 * ((n_log + 7) / 8));
+  DecodeArgs none{};
+  hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, true>), grid, dim3(NW * 64), 0, s, none, a);
   return hipGetLastError();
 }
 
@@ -863,9 +721,24 @@ hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel, dim3(a.rows), dim3(128), 0, s, a);
+template <int D>
+hipError_t merge_launch(const MergeArgs& a, hipStream_t s) {
+  constexpr int D4 = D / 4;
+  constexpr int NT = D4 > 64 ? D4 : 64;
+  constexpr int R = NT / D4;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3((a.rows + R - 1) / R), dim3(NT), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
+  switch (a.D) {
+    case 32: return merge_launch<32>(a, s);
+    case 64: return merge_launch<64>(a, s);
+    case 128: return merge_launch<128>(a, s);
+    case 256: return merge_launch<256>(a, s);
+    case 512: return merge_launch<512>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 #define G4_DISPATCH(FN, ARGS)                                             \
@@ -885,9 +758,8 @@ hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, int bat
 #undef G4_ARGS
 }
 
-hipError_t launch_prefill(int head_dim, bool k_eq_v, const PrefillArgs& a, int batch,
-                          hipStream_t s) {
-#define G4_ARGS a, batch, s
+hipError_t launch_prefill(int head_dim, bool k_eq_v, const PrefillArgs& a, hipStream_t s) {
+#define G4_ARGS a, s
   G4_DISPATCH(prefill_launch, G4_ARGS)
 #undef G4_ARGS
 }

@@ -8,6 +8,7 @@
 // follows section 5 of the same page.
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -95,22 +96,6 @@ void decode_splits(int keys_max, int KB, int pairs, int wgs_per_cu, int* blocks_
   int bps = ceil_div(nb_max, ns);
   *blocks_per_split = bps;
   *n_splits = ceil_div(nb_max, bps);
-}
-
-void prefill_splits(int span, int pairs, int KT, int max_splits, int* split_keys,
-                    int* n_splits) {
-  span += KT - 1;  // alignment slack of the first split
-  const int target_wgs = 512;
-  int ns = ceil_div(target_wgs, pairs);
-  int max_by_len = ceil_div(span, 2 * KT);
-  if (ns > max_by_len) ns = max_by_len;
-  if (ns > max_splits) ns = max_splits;
-  if (ns < 1) ns = 1;
-  int sk = ceil_div(ceil_div(span, ns), KT) * KT;
-  if (sk < KT) sk = KT;
-  *split_keys = sk;
-  *n_splits = ceil_div(span, sk);
-  if (*n_splits < 1) *n_splits = 1;
 }
 
 // Split results are merged by the last workgroup to arrive when the merge is
@@ -219,15 +204,11 @@ int32_t g4attn_stack_create(const g4attn_layer_desc* layers, int32_t n_layers, i
     const g4attn_layer_desc& d = st->L[i].d;
     const int G = d.n_q_heads / d.n_kv_heads;
     const uint64_t hblk = (uint64_t)(G + 15) / 16;
-    const uint64_t rows_p = (uint64_t)max_chunk * G;
-    const uint64_t rblk = (rows_p + g4::kPrefillRows - 1) / g4::kPrefillRows;
     const uint64_t c_d = (uint64_t)max_batch * d.n_kv_heads * hblk;
-    const uint64_t c_p = (uint64_t)max_batch * d.n_kv_heads * rblk;
     const uint64_t r_d = (uint64_t)max_batch * d.n_q_heads * g4::kMaxDecodeSplits;
-    const uint64_t r_p = (uint64_t)max_batch * d.n_kv_heads * rows_p * g4::kMaxPrefillSplits;
-    ctr = std::max(ctr, std::max(c_d, c_p));
-    ml = std::max(ml, 2 * std::max(r_d, r_p));
-    of = std::max(of, (uint64_t)d.head_dim * std::max(r_d, r_p));
+    ctr = std::max(ctr, c_d);
+    ml = std::max(ml, 2 * r_d);
+    of = std::max(of, (uint64_t)d.head_dim * r_d);
   }
   st->ctr_count = ctr;
   st->ml_floats = ml;
@@ -370,7 +351,7 @@ int32_t g4attn_decode(const g4attn_stack* st, int32_t layer, const void* q,
   const int nh = G < 16 ? G : 16;
   const int keys_max = d.window > 0 && d.window < max_seq_len ? d.window : max_seq_len;
   g4::DecodeArgs a;
-  const int wgs_per_cu = d.head_dim >= 512 ? 1 : 2;
+  const int wgs_per_cu = (d.head_dim >= 512 && !d.k_eq_v) ? 1 : 2;
   const int KB = g4::decode_block(d.k_eq_v != 0);
   decode_splits(keys_max, KB, batch * d.n_kv_heads * n_hblk, wgs_per_cu, &a.blocks_per_split,
                 &a.n_splits);
@@ -402,7 +383,6 @@ int32_t g4attn_decode(const g4attn_stack* st, int32_t layer, const void* q,
     m.rows = batch * d.n_q_heads;
     m.n_splits = a.n_splits;
     m.D = d.head_dim;
-    m.prefill = 0;
     m.n_q = d.n_q_heads;
     m.seq_lens = seq_lens;
     m.window = d.window;
@@ -431,27 +411,19 @@ int32_t g4attn_prefill(const g4attn_stack* st, int32_t layer, const void* q,
   if (!st->cache || !st->ws) return fail(G4ATTN_ERR_UNBOUND, "cache/workspace not bound");
   const LayerPlan& p = st->L[layer];
   const g4attn_layer_desc& d = p.d;
-  if ((int64_t)batch * d.n_kv_heads > 65535)
-    return fail(G4ATTN_ERR_UNSUPPORTED, "batch x n_kv_heads %lld exceeds the launch grid",
-                (long long)batch * d.n_kv_heads);
   const int G = d.n_q_heads / d.n_kv_heads;
   g4::PrefillArgs a;
   a.rows = n_tok * G;
   a.n_rowblk = (a.rows + g4::kPrefillRows - 1) / g4::kPrefillRows;
-  const int full = max_start_pos + n_tok;
-  const int span = d.window > 0 && d.window + n_tok - 1 < full ? d.window + n_tok - 1 : full;
-  prefill_splits(span, batch * d.n_kv_heads * a.n_rowblk, g4::prefill_tile(d.head_dim),
-                 g4::kMaxPrefillSplits, &a.split_keys, &a.n_splits);
-  a.merge_in_kernel = (int64_t)a.n_splits * g4::kPrefillRows * d.head_dim * 4 <=
-                              kInKernelMergeBytes ? 1 : 0;
+  if ((int64_t)batch * d.n_kv_heads * a.n_rowblk + 7 > (int64_t)INT32_MAX)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "prefill grid of %lld workgroups too large",
+                (long long)batch * d.n_kv_heads * a.n_rowblk);
   a.q = static_cast<const uint16_t*>(q);
   a.kp = reinterpret_cast<const uint16_t*>(st->cache + p.k_off);
   a.vp = reinterpret_cast<const uint16_t*>(st->cache + p.v_off);
   a.start_pos = start_pos;
   a.out = static_cast<uint16_t*>(out);
-  a.counters = reinterpret_cast<int32_t*>(st->ws + st->ws_ctr_off);
-  a.part_ml = reinterpret_cast<float*>(st->ws + st->ws_ml_off);
-  a.part_o = reinterpret_cast<float*>(st->ws + st->ws_o_off);
+  a.batch = batch;
   a.n_q = d.n_q_heads;
   a.n_kv = d.n_kv_heads;
   a.G = G;
@@ -460,24 +432,8 @@ int32_t g4attn_prefill(const g4attn_stack* st, int32_t layer, const void* q,
   a.window = d.window;
   a.kv_max = st->kv_max;
   a.scale_log2 = d.scale * 1.4426950408889634f;
-  hipError_t e = g4::launch_prefill(d.head_dim, d.k_eq_v != 0, a, batch,
+  hipError_t e = g4::launch_prefill(d.head_dim, d.k_eq_v != 0, a,
                                     static_cast<hipStream_t>(stream));
-  if (e == hipSuccess && a.n_splits > 1 && !a.merge_in_kernel) {
-    g4::MergeArgs m{};
-    m.part_o = a.part_o;
-    m.part_ml = a.part_ml;
-    m.out = a.out;
-    m.rows = batch * d.n_kv_heads * a.rows;
-    m.n_splits = a.n_splits;
-    m.D = d.head_dim;
-    m.prefill = 1;
-    m.T = n_tok;
-    m.G = G;
-    m.n_q = d.n_q_heads;
-    m.n_kv = d.n_kv_heads;
-    m.rows_per_group = a.rows;
-    e = g4::launch_merge(m, static_cast<hipStream_t>(stream));
-  }
   if (e != hipSuccess) return fail(G4ATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();
 }
