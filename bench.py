@@ -15,7 +15,7 @@ Also reported on the same line:
                 workload, on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-prefill] [--long]
+                       [--no-prefill] [--copy-calib]
 """
 
 from __future__ import annotations
@@ -45,6 +45,31 @@ def kv_bytes(wl, layer):
     for L in wl.seq_lens:
         keys += min(L, d.window) if d.window > 0 else L
     return keys * d.n_kv_heads * d.head_dim * 2 * (1 if d.k_eq_v else 2)
+
+
+DOMINANT_KERNEL = "attend_kernel<256, false, 4, false, 1>"
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "attend_12b_hbm_bytes.md")
+KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_gemma_amd", "csrc", "kernels.hip")
+
+
+def counter_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` (calibrated FETCH_SIZE + WRITE_SIZE)
+    from the committed rocprofv3 summary, or None when that summary was taken
+    on a different kernel source than the one built now."""
+    import hashlib
+
+    try:
+        text = open(COUNTER_SUMMARY).read()
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    if f"kernels.hip sha256[:16]: {src}" not in text:
+        return None
+    for row in text.splitlines():
+        cells = [c.strip() for c in row.strip().strip("|").split("|")]
+        if len(cells) == 6 and cells[0] == kernel:
+            return int(round((float(cells[3]) + float(cells[5])) * 1e6))
+    return None
 
 
 def prefill_flops(wl, layer):
@@ -270,13 +295,13 @@ def main():
             "global_layer_decode_gbs": round(dec["glob"]["gbs"], 1),
         },
         "roofline": {
-            "kernel": "decode_kernel<256,false> (sliding layer)",
+            "kernel": DOMINANT_KERNEL + " (sliding-layer decode)",
             "bound": "hbm",
             "achieved": round(dom["gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": counter_traffic(DOMINANT_KERNEL),
             "us_per_launch": round(dom["ms"] * 1e3, 2),
             "bytes_per_launch": dom["bytes"],
         },

@@ -30,6 +30,19 @@ constexpr int kPrefillRows = 16;
 
 inline int decode_block(bool k_eq_v) { return k_eq_v ? 16 : 32; }
 
+// Key blocks each decode wave keeps in flight (its register ring).  Deeper
+// rings need one wave per SIMD, which halves the resident workgroups; on
+// MI355X that costs more than the extra loads in flight gain, so every layer
+// type uses a single block.
+__host__ __device__ constexpr int decode_prefetch(int head_dim, bool k_eq_v) {
+  return (void)head_dim, (void)k_eq_v, 1;
+}
+// Waves per SIMD a kernel instance is built for (2 = up to 256 registers per
+// lane, 1 = up to 512 with the accumulation registers).
+__host__ __device__ constexpr int waves_per_simd(int head_dim, bool k_eq_v, int prefetch) {
+  return prefetch > 1 || (head_dim >= 512 && !k_eq_v) ? 1 : 2;
+}
+
 // Byte offsets of element d of the K row / V row in one segment.
 __host__ __device__ inline int64_t k_elem_offset(int64_t slot, int d, int D) {
   const int64_t blk = slot / 16, kk = slot % 16;

@@ -219,15 +219,18 @@ __device__ void merge_rows_coherent(const float* part_o, const float* part_ml, s
 
 // Stand-alone version for large decode merges (a kernel boundary separates
 // writer and reader, so ordinary loads see the partials).  A workgroup takes
-// R = max(64, D/4) / (D/4) rows; every thread owns one 4-dim slice of a row
-// and issues the loads of all of that row's splits at once, so the merge
-// costs two memory round trips.
+// R = max(64, D/4) / (D/4) rows; every thread owns one 4-dim slice of a row.
+// The sequence lengths and every (m, l) pair are fetched together, then the
+// partial outputs of up to 32 splits at once, so the merge costs two memory
+// round trips.
 template <int D>
 __global__ __launch_bounds__(D / 4 > 64 ? D / 4 : 64) void merge_kernel(MergeArgs a) {
   constexpr int D4 = D / 4;
   constexpr int NT = D4 > 64 ? D4 : 64;
   constexpr int R = NT / D4;
-  constexpr int CH = 16;  // splits loaded per batch
+  constexpr int CH = 32;                                  // splits loaded per batch
+  constexpr int PER = (R * kMaxDecodeSplits + NT - 1) / NT;  // (m, l) pairs per thread
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   __shared__ float wgt[R][kMaxDecodeSplits];
   __shared__ float lval[R][kMaxDecodeSplits];
   __shared__ float s_inv[R];
@@ -235,7 +238,17 @@ __global__ __launch_bounds__(D / 4 > 64 ? D / 4 : 64) void merge_kernel(MergeArg
   const int tid = threadIdx.x;
   const size_t row0 = (size_t)blockIdx.x * R;
 
-  // splits in use and output offset of each row of this workgroup
+  // (m, l) of every split slot of the workgroup's rows, issued before the
+  // lengths that say which slots are in use
+  f32x2 mlv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid + i * NT;
+    const int r = idx / a.n_splits;
+    if (r < R && row0 + r < (size_t)a.rows)
+      mlv[i] = *reinterpret_cast<const f32x2*>(a.part_ml + ((row0 + r) * a.n_splits +
+                                                            (idx - r * a.n_splits)) * 2);
+  }
   if (tid < R) {
     const size_t row = row0 + tid;
     int n_used = 0;
@@ -250,14 +263,13 @@ __global__ __launch_bounds__(D / 4 > 64 ? D / 4 : 64) void merge_kernel(MergeArg
     }
     s_used[tid] = n_used;
   }
-  __syncthreads();
-  // (m, l) pairs: one per thread, all rows of the workgroup at once
-  for (int i = tid; i < R * a.n_splits; i += NT) {
-    const int r = i / a.n_splits, s = i - (i / a.n_splits) * a.n_splits;
-    if (s < s_used[r]) {
-      const float* ml = a.part_ml + ((row0 + r) * a.n_splits + s) * 2;
-      wgt[r][s] = ml[0];
-      lval[r][s] = ml[1];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid + i * NT;
+    const int r = idx / a.n_splits;
+    if (r < R && row0 + r < (size_t)a.rows) {
+      wgt[r][idx - r * a.n_splits] = mlv[i][0];
+      lval[r][idx - r * a.n_splits] = mlv[i][1];
     }
   }
   __syncthreads();
@@ -335,7 +347,10 @@ struct Shape {
   static constexpr int TRH = KS >= 2 ? KS / 2 : KS;
   static constexpr int NPH = KS / TRH;
   static constexpr int TR_ELEMS = KEQV ? TRH * 512 : 0;  // per-wave transpose area
-  static constexpr int RED_BYTES = 16 * D * 4;            // cross-wave reduction
+  // cross-wave reduction rows are padded by 4 floats so that the 16 rows a
+  // wave writes at once start on different LDS banks
+  static constexpr int RED_STRIDE = D + 4;
+  static constexpr int RED_BYTES = 16 * RED_STRIDE * 4;
   static constexpr int MERGE_BYTES = (2 * 16 * kMaxDecodeSplits + 16) * 4;
   static constexpr int TR_BYTES = NW * TR_ELEMS * 2;
   static constexpr int A_BYTES = TR_BYTES > RED_BYTES ? TR_BYTES : RED_BYTES;
@@ -344,8 +359,8 @@ struct Shape {
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D, bool KEQV, int NW, bool PREFILL>
-__global__ __launch_bounds__(NW * 64, (D >= 512 && !KEQV) ? 1 : 2) void attend_kernel(
+template <int D, bool KEQV, int NW, bool PREFILL, int PF>
+__global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PF)) void attend_kernel(
     DecodeArgs da, PrefillArgs pa) {
   using S = Shape<D, KEQV, NW>;
   constexpr int KB = S::KB, NSB = S::NSB, KS = S::KS, NDB = S::NDB;
@@ -445,29 +460,34 @@ __global__ __launch_bounds__(NW * 64, (D >= 512 && !KEQV) ? 1 : 2) void attend_k
   const uint16_t* kseg = kp + seg;
   const uint16_t* vseg = vp + seg;
 
-  // ---- block loads: the next block's K is loaded as soon as the registers
-  // it lands in are free, so it overlaps the rest of the current block ----
-  u32x4 kreg[NSB][KS];
-  u32x4 vreg[KEQV ? 1 : NDB];
-  auto load_k = [&](int blk) {
+  // ---- block loads: a wave keeps PF blocks in flight in a register ring;
+  // a block's successor in its ring slot is loaded as soon as the registers
+  // are free, so it overlaps the rest of the current block ----
+  u32x4 kreg[PF][NSB][KS];
+  u32x4 vreg[PF][KEQV ? 1 : NDB];
+  auto load_k = [&](int r, int blk) {
     const int slot0 = (blk * KB) % cap;
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        kreg[sb][s] = ldg16(kseg + ((size_t)(slot0 / 16 + sb) * KS + s) * 512 + lane * 8);
+        kreg[r][sb][s] = ldg16(kseg + ((size_t)(slot0 / 16 + sb) * KS + s) * 512 + lane * 8);
   };
-  auto load_v = [&](int blk) {
+  auto load_v = [&](int r, int blk) {
     if constexpr (!KEQV) {
       const int slot0 = (blk * KB) % cap;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        vreg[db] = ldg16(vseg + ((size_t)(slot0 / 32) * NDB + db) * 512 + lane * 8);
+        vreg[r][db] = ldg16(vseg + ((size_t)(slot0 / 32) * NDB + db) * 512 + lane * 8);
     }
   };
-  if (n_keys > 0 && blk_first + w < blk_end) {
-    load_k(blk_first + w);
-    load_v(blk_first + w);
+  if (n_keys > 0) {
+#pragma unroll
+    for (int r = 0; r < PF; ++r)
+      if (blk_first + w + r * NW < blk_end) {
+        load_k(r, blk_first + w + r * NW);
+        load_v(r, blk_first + w + r * NW);
+      }
   }
 
   // queries as the B operand of S^T = K Q^T (column c16 = row, k-slots =
@@ -485,9 +505,14 @@ __global__ __launch_bounds__(NW * 64, (D >= 512 && !KEQV) ? 1 : 2) void attend_k
   uint16_t* tr = reinterpret_cast<uint16_t*>(lds) + w * S::TR_ELEMS;  // k_eq_v only
 
   if (n_keys > 0) {
-    for (int blk = blk_first + w; blk < blk_end; blk += NW) {
+    for (int base = blk_first + w; base < blk_end; base += NW * PF) {
+#pragma unroll
+    for (int r = 0; r < PF; ++r) {
+      const int blk = base + r * NW;
+      if (blk >= blk_end) break;
+      const int nxt = blk + NW * PF;  // next block of this ring slot
+      const bool has_next = nxt < blk_end;
       const int pos0 = blk * KB;
-      const bool has_next = blk + NW < blk_end;
       const bool full = pos0 >= full_lo && pos0 + KB <= full_hi;
       const bool vfull = pos0 >= r_beg && pos0 + KB <= r_end;
 
@@ -495,18 +520,32 @@ __global__ __launch_bounds__(NW * 64, (D >= 512 && !KEQV) ? 1 : 2) void attend_k
       // barrier keeps the query reads from LDS here instead of hoisting the
       // whole query operand into registers for the loop.
       asm volatile("" ::: "memory");
+      // two independent accumulation chains per score block keep the
+      // matrix core busy while each MFMA's result is still in flight
+      constexpr int NCH = KS >= 2 ? 2 : 1;
       f32x4 sacc[NSB];
+      {
+        f32x4 sch[NSB][NCH];
 #pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) {
-        sacc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) sch[sb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           const bf16x8 qf = *reinterpret_cast<const bf16x8*>(&Qs[(s * 64 + lane) * 8]);
-          sacc[sb] = mfma32(as_bf16x8(kreg[sb][s]), qf, sacc[sb]);
+#pragma unroll
+          for (int sb = 0; sb < NSB; ++sb)
+            sch[sb][s % NCH] = mfma32(as_bf16x8(kreg[r][sb][s]), qf, sch[sb][s % NCH]);
+        }
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
+          sacc[sb] = sch[sb][0];
+#pragma unroll
+          for (int c = 1; c < NCH; ++c) sacc[sb] += sch[sb][c];
         }
       }
       if constexpr (!KEQV) {
-        if (has_next) load_k(blk + NW);
+        if (has_next) load_k(r, nxt);
       }
       float lmax = kNegInf;
 #pragma unroll
@@ -549,7 +588,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 512 && !KEQV) ? 1 : 2) void attend_k
         }
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          bf16x8 vf = as_bf16x8(vreg[db]);
+          bf16x8 vf = as_bf16x8(vreg[r][db]);
           if (!vfull) {  // values of keys outside the range must not reach the MFMA
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -560,7 +599,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 512 && !KEQV) ? 1 : 2) void attend_k
           }
           oacc[db] = mfma32(vf, pf, oacc[db]);
         }
-        if (has_next) load_v(blk + NW);
+        if (has_next) load_v(r, nxt);
       } else {
         // the K block doubles as V: each phase stages TRH of its sub-tiles in
         // this wave's LDS area in operand order; one transposing 64-bit read
@@ -571,7 +610,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 512 && !KEQV) ? 1 : 2) void attend_k
         for (int ph = 0; ph < S::NPH; ++ph) {
 #pragma unroll
           for (int s = 0; s < S::TRH; ++s)
-            *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[0][ph * S::TRH + s];
+            *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[r][0][ph * S::TRH + s];
 #pragma unroll
           for (int dbl = 0; dbl < NDB / S::NPH; ++dbl) {
             const int dd = 16 * dbl + 4 * (c16 & 3);  // dim within the staged sub-tiles
@@ -590,8 +629,9 @@ __global__ __launch_bounds__(NW * 64, (D >= 512 && !KEQV) ? 1 : 2) void attend_k
             oacc[db] = mfma16(vf, pb[0], oacc[db]);
           }
         }
-        if (has_next) load_k(blk + NW);
+        if (has_next) load_k(r, nxt);
       }
+    }
     }
   }
 
@@ -616,12 +656,13 @@ __global__ __launch_bounds__(NW * 64, (D >= 512 && !KEQV) ? 1 : 2) void attend_k
     hL[tid] = Lh;
   }
   const float mine = fast_exp2(m_run - M_use);
-  float* red = reinterpret_cast<float*>(lds);  // [16][D]
+  constexpr int RS = S::RED_STRIDE;
+  float* red = reinterpret_cast<float*>(lds);  // [16][RS]
   for (int step = NW - 1; step >= 0; --step) {
     if (w == step && c16 < nrows) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        float* p = red + c16 * D + 16 * db + 4 * q4;
+        float* p = red + c16 * RS + 16 * db + 4 * q4;
         f32x4 v = oacc[db] * mine;
         if (step != NW - 1) v += *reinterpret_cast<f32x4*>(p);
         *reinterpret_cast<f32x4*>(p) = v;
@@ -636,7 +677,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 512 && !KEQV) ? 1 : 2) void attend_k
       const int r = idx / D4;
       const int d = 4 * (idx - r * D4);
       const float il = hL[r] > 0.f ? 1.f / hL[r] : 0.f;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(red + r * D + d);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(red + r * RS + d);
       bf16x4 o;
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j] = (__bf16)(v[j] * il);
@@ -660,7 +701,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 512 && !KEQV) ? 1 : 2) void attend_k
     for (int idx = tid; idx < nrows * D4; idx += NT) {
       const int h = idx / D4;
       const int d = 4 * (idx - h * D4);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(red + h * D + d);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(red + h * RS + d);
       float* dst = a.part_o + (prow0 + (size_t)h * a.n_splits) * D + d;
       if (a.merge_in_kernel)
         st16_coherent(dst, v);
@@ -698,7 +739,8 @@ template <int D, bool KEQV>
 hipError_t decode_launch(const DecodeArgs& a, int batch, hipStream_t s) {
   dim3 grid(a.n_splits, a.n_kv * a.n_hblk, batch);
   PrefillArgs none{};
-  hipLaunchKernelGGL((attend_kernel<D, KEQV, 4, false>), grid, dim3(256), 0, s, a, none);
+  hipLaunchKernelGGL((attend_kernel<D, KEQV, 4, false, decode_prefetch(D, KEQV)>), grid, dim3(256),
+                     0, s, a, none);
   return hipGetLastError();
 }
 
@@ -709,7 +751,7 @@ hipError_t prefill_launch(const PrefillArgs& a, hipStream_t s) {
   const int n_log = a.n_rowblk * a.n_kv * a.batch;
   dim3 grid(8 * ((n_log + 7) / 8));
   DecodeArgs none{};
-  hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, true>), grid, dim3(NW * 64), 0, s, none, a);
+  hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, true, 1>), grid, dim3(NW * 64), 0, s, none, a);
   return hipGetLastError();
 }
 
