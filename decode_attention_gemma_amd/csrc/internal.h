@@ -30,17 +30,13 @@ constexpr int kPrefillRows = 16;
 
 inline int decode_block(bool k_eq_v) { return k_eq_v ? 16 : 32; }
 
-// Key blocks each decode wave keeps in flight (its register ring).  Deeper
-// rings need one wave per SIMD, which halves the resident workgroups; on
-// MI355X that costs more than the extra loads in flight gain, so every layer
-// type uses a single block.
-__host__ __device__ constexpr int decode_prefetch(int head_dim, bool k_eq_v) {
-  return (void)head_dim, (void)k_eq_v, 1;
-}
-// Waves per SIMD a kernel instance is built for (2 = up to 256 registers per
-// lane, 1 = up to 512 with the accumulation registers).
-__host__ __device__ constexpr int waves_per_simd(int head_dim, bool k_eq_v, int prefetch) {
-  return prefetch > 1 || (head_dim >= 512 && !k_eq_v) ? 1 : 2;
+// Waves per SIMD an attention kernel instance is built for: 2 (up to 256
+// registers per lane), or 1 where one wave needs more: head_dim 512 without
+// k_eq_v (its V block and accumulators alone take 256), or a ring of more
+// than one key block in flight.  A decode workgroup has one wave per SIMD, so
+// this is also its workgroups per CU.
+__host__ __device__ constexpr int waves_per_simd(int head_dim, bool k_eq_v, int ring = 1) {
+  return ring > 1 || (head_dim >= 512 && !k_eq_v) ? 1 : 2;
 }
 
 // Byte offsets of element d of the K row / V row in one segment.

@@ -24,6 +24,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
+#include <type_traits>
+
 #include "internal.h"
 
 namespace g4 {
@@ -36,6 +39,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
+// log2 of the largest probability the lazily rescaled online softmax admits
+constexpr float kLazyRescale = 8.f;
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -47,6 +52,15 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Scheduling fence: the values in `acc` count as read and rewritten here, and
+// memory operations do not move across it.  Loads placed after it therefore
+// stay after the instructions that produced `acc`.
+template <int N>
+__device__ __forceinline__ void pin_after(f32x4 (&acc)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(acc[i])::"memory");
+}
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -337,14 +351,15 @@ __global__ __launch_bounds__(D / 4 > 64 ? D / 4 : 64) void merge_kernel(MergeArg
 // results exist.  The grid is laid out so that the row blocks of one
 // (sequence, KV head) run on the same XCD and share its L2.
 
-template <int D, bool KEQV, int NW>
+template <int D, bool KEQV, int NW, int PF, bool SAG>
 struct Shape {
   static constexpr int KB = KEQV ? 16 : 32;  // keys per block
   static constexpr int NSB = KB / 16;        // 16-key score blocks per block
   static constexpr int KS = D / 32;          // 1 KiB K sub-tiles per 16 keys
   static constexpr int NDB = D / 16;         // 16-dim output blocks
-  // k_eq_v: the block is transposed through LDS in NPH phases of TRH sub-tiles
-  static constexpr int TRH = KS >= 2 ? KS / 2 : KS;
+  // k_eq_v: the block is transposed through LDS in NPH phases of TRH
+  // sub-tiles, or staged whole while the scores are computed (SAG)
+  static constexpr int TRH = SAG || KS < 2 ? KS : KS / 2;
   static constexpr int NPH = KS / TRH;
   static constexpr int TR_ELEMS = KEQV ? TRH * 512 : 0;  // per-wave transpose area
   // cross-wave reduction rows are padded by 4 floats so that the 16 rows a
@@ -362,7 +377,12 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 template <int D, bool KEQV, int NW, bool PREFILL, int PF>
 __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PF)) void attend_kernel(
     DecodeArgs da, PrefillArgs pa) {
-  using S = Shape<D, KEQV, NW>;
+  // k_eq_v prefill stages each K sub-tile for the V^T transpose as soon as
+  // its score MFMA has read it, and reloads the register with the next
+  // block's sub-tile at once (a whole block of prefetch distance; the staging
+  // area then holds a full block per wave)
+  constexpr bool SAG = PREFILL && KEQV;
+  using S = Shape<D, KEQV, NW, PF, SAG>;
   constexpr int KB = S::KB, NSB = S::NSB, KS = S::KS, NDB = S::NDB;
   constexpr int D4 = D / 4;
   constexpr int NT = NW * 64;
@@ -460,18 +480,27 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PF)) void attend_k
   const uint16_t* kseg = kp + seg;
   const uint16_t* vseg = vp + seg;
 
-  // ---- block loads: a wave keeps PF blocks in flight in a register ring;
-  // a block's successor in its ring slot is loaded as soon as the registers
-  // are free, so it overlaps the rest of the current block ----
-  u32x4 kreg[PF][NSB][KS];
+  // ---- block loads.  The next block's K (and V) is loaded as soon as the
+  // registers it lands in are free, so it overlaps the rest of the current
+  // block.  With a V plane the wave's last block is peeled off the loop:
+  // inside the loop the prefetch is then unconditional, which lets the
+  // compiler wait for exactly the loads an instruction needs (memory counters
+  // complete in issue order; after a conditional prefetch of the next K, the
+  // wait for the current V would also cover the first of those loads) ----
+  u32x4 kreg[PF][NSB][KS];  // PF > 1: a ring of blocks blk, blk + NW, ...
   u32x4 vreg[PF][KEQV ? 1 : NDB];
-  auto load_k = [&](int r, int blk) {
+  // this lane's address in the K sub-tile 0 of a block (sub-tile s of score
+  // block sb follows at (sb * KS + s) * 512 elements)
+  auto kblock = [&](int blk) {
     const int slot0 = (blk * KB) % cap;
+    return kseg + (size_t)(slot0 / 16) * KS * 512 + lane * 8;
+  };
+  auto load_k = [&](int r, int blk) {
+    const uint16_t* kb = kblock(blk);
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        kreg[r][sb][s] = ldg16(kseg + ((size_t)(slot0 / 16 + sb) * KS + s) * 512 + lane * 8);
+      for (int s = 0; s < KS; ++s) kreg[r][sb][s] = ldg16(kb + (sb * KS + s) * 512);
   };
   auto load_v = [&](int r, int blk) {
     if constexpr (!KEQV) {
@@ -481,14 +510,14 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PF)) void attend_k
         vreg[r][db] = ldg16(vseg + ((size_t)(slot0 / 32) * NDB + db) * 512 + lane * 8);
     }
   };
-  if (n_keys > 0) {
+  const int n_mine = n_keys > 0 && blk_first + w < blk_end
+                         ? (blk_end - (blk_first + w) + NW - 1) / NW : 0;  // blocks of this wave
 #pragma unroll
-    for (int r = 0; r < PF; ++r)
-      if (blk_first + w + r * NW < blk_end) {
-        load_k(r, blk_first + w + r * NW);
-        load_v(r, blk_first + w + r * NW);
-      }
-  }
+  for (int r = 0; r < PF; ++r)
+    if (r < n_mine) {
+      load_k(r, blk_first + w + r * NW);
+      load_v(r, blk_first + w + r * NW);
+    }
 
   // queries as the B operand of S^T = K Q^T (column c16 = row, k-slots =
   // dims), kept in LDS in operand order: sub-tile s, lane L at (s*64 + L)*8
@@ -504,134 +533,197 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PF)) void attend_k
   float l_run = 0.f;
   uint16_t* tr = reinterpret_cast<uint16_t*>(lds) + w * S::TR_ELEMS;  // k_eq_v only
 
-  if (n_keys > 0) {
-    for (int base = blk_first + w; base < blk_end; base += NW * PF) {
-#pragma unroll
-    for (int r = 0; r < PF; ++r) {
-      const int blk = base + r * NW;
-      if (blk >= blk_end) break;
-      const int nxt = blk + NW * PF;  // next block of this ring slot
-      const bool has_next = nxt < blk_end;
-      const int pos0 = blk * KB;
-      const bool full = pos0 >= full_lo && pos0 + KB <= full_hi;
-      const bool vfull = pos0 >= r_beg && pos0 + KB <= r_end;
+  // one key block, held in ring slot r; `pf` (a bool, or std::true_type /
+  // std::false_type) says whether the slot's next block (blk + NW * PF) is
+  // loaded
+  auto block = [&](const int blk, const int r, auto pf) {
+    const bool PFX = pf;  // a compile-time constant where the caller passes a type
+    const int nxt = blk + NW * PF;
+    // the next block's address, computed before any compiler barrier below
+    // (those make captured values be reloaded)
+    const uint16_t* const kbn = kblock(nxt);
+    const int pos0 = blk * KB;
+    const bool full = pos0 >= full_lo && pos0 + KB <= full_hi;
+    const bool vfull = pos0 >= r_beg && pos0 + KB <= r_end;
 
-      // scores, mask, online softmax (lane's column c16 = row).  The compiler
-      // barrier keeps the query reads from LDS here instead of hoisting the
-      // whole query operand into registers for the loop.
-      asm volatile("" ::: "memory");
-      // two independent accumulation chains per score block keep the
-      // matrix core busy while each MFMA's result is still in flight
-      constexpr int NCH = KS >= 2 ? 2 : 1;
-      f32x4 sacc[NSB];
-      {
-        f32x4 sch[NSB][NCH];
-#pragma unroll
-        for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-          for (int c = 0; c < NCH; ++c) sch[sb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const bf16x8 qf = *reinterpret_cast<const bf16x8*>(&Qs[(s * 64 + lane) * 8]);
-#pragma unroll
-          for (int sb = 0; sb < NSB; ++sb)
-            sch[sb][s % NCH] = mfma32(as_bf16x8(kreg[r][sb][s]), qf, sch[sb][s % NCH]);
-        }
-#pragma unroll
-        for (int sb = 0; sb < NSB; ++sb) {
-          sacc[sb] = sch[sb][0];
-#pragma unroll
-          for (int c = 1; c < NCH; ++c) sacc[sb] += sch[sb][c];
-        }
-      }
-      if constexpr (!KEQV) {
-        if (has_next) load_k(r, nxt);
-      }
-      float lmax = kNegInf;
-#pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kpos = pos0 + 16 * sb + 4 * q4 + j;
-          const bool ok = full ? row_ok : (kpos >= row_lo && kpos < row_hi);
-          sacc[sb][j] = ok ? sacc[sb][j] * scale_log2 : kNegInf;
-          lmax = fmaxf(lmax, sacc[sb][j]);
-        }
-      }
-      lmax = fmaxf(lmax, __shfl_xor(lmax, 16));
-      lmax = fmaxf(lmax, __shfl_xor(lmax, 32));
-      const float m_new = fmaxf(m_run, lmax);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
-      bf16x4 pb[NSB];
-      float psum = 0.f;
+    // scores, mask, online softmax (lane's column c16 = row).  The compiler
+    // barrier keeps the query reads from LDS here instead of hoisting the
+    // whole query operand into registers for the loop.  Two independent
+    // accumulation chains per score block keep the matrix core busy while
+    // each MFMA's result is still in flight.
+    asm volatile("" ::: "memory");
+    constexpr int NCH = KS >= 2 ? 2 : 1;
+    f32x4 sacc[NSB];
+    {
+      f32x4 sch[NSB][NCH];
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const __bf16 p = (__bf16)fast_exp2(sacc[sb][j] - m_use);
-          pb[sb][j] = p;
-          psum += (float)p;
+        for (int c = 0; c < NCH; ++c) sch[sb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 qf = *reinterpret_cast<const bf16x8*>(&Qs[(s * 64 + lane) * 8]);
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb)
+          sch[sb][s % NCH] = mfma32(as_bf16x8(kreg[r][sb][s]), qf, sch[sb][s % NCH]);
+        if constexpr (SAG) {
+          *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[r][0][s];
+          if (PFX) {
+            asm volatile("" ::: "memory");  // after the staging write
+            kreg[r][0][s] = ldg16(kbn + s * 512);
+          }
         }
-      l_run = l_run * alpha + psum;
+      }
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        sacc[sb] = sch[sb][0];
+#pragma unroll
+        for (int c = 1; c < NCH; ++c) sacc[sb] += sch[sb][c];
+      }
+    }
+    if (!KEQV && PFX) {
+      // the next K lands in the registers the score MFMAs just read: keep
+      // its loads after them (hoisting them would need a second set)
+      pin_after(sacc);
+      load_k(r, nxt);
+    }
+    // visible keys of this lane's row within the block (bitwise, no branches)
+    const int vis_lo = full ? INT_MIN : row_lo;
+    const int vis_hi = full ? INT_MAX : row_hi;
+    float lmax = kNegInf;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kpos = pos0 + 16 * sb + 4 * q4 + j;
+        const bool ok = row_ok & (kpos >= vis_lo) & (kpos < vis_hi);
+        sacc[sb][j] = ok ? sacc[sb][j] * scale_log2 : kNegInf;
+        lmax = fmaxf(lmax, sacc[sb][j]);
+      }
+    }
+    lmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+    lmax = fmaxf(lmax, __shfl_xor(lmax, 32));
+    // Lazy rescaling: the reference max m_run moves only when some row's
+    // block max exceeds it by more than 2^8, so probabilities stay <= 256
+    // (exact enough in fp32 and bf16) and most blocks skip rescaling the
+    // output accumulators.  The decision is uniform across the wave.
+    // (Only the multiplies sit under the branch: with more inside it the
+    // register allocation no longer fits.)
+    const bool need = __ballot(lmax > m_run + kLazyRescale) != 0ull;
+    const float m_new = need ? fmaxf(m_run, lmax) : m_run;
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
+    if (need) {
 #pragma unroll
       for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
+    }
+    bf16x4 pb[NSB];
+    float psum = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const __bf16 p = (__bf16)fast_exp2(sacc[sb][j] - m_use);
+        pb[sb][j] = p;
+        psum += (float)p;
+      }
+    l_run += psum;
 
-      if constexpr (!KEQV) {
-        // P^T as the B operand: k-slot j <-> key 4q+j (j<4) / 16+4q+j-4
-        bf16x8 pf;
+    // Values of keys outside [r_beg, r_end) must not reach the MFMA (their
+    // probabilities are zero, but the slots may hold any bit pattern).  The
+    // mask is per lane and k-slot; it is applied with bitwise ands.
+    if constexpr (!KEQV) {
+      // P^T as the B operand: k-slot j <-> key 4q+j (j<4) / 16+4q+j-4
+      bf16x8 pf8;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pf[j] = pb[0][j];
-          pf[4 + j] = pb[1][j];
-        }
+      for (int j = 0; j < 4; ++j) {
+        pf8[j] = pb[0][j];
+        pf8[4 + j] = pb[1][j];
+      }
+      if (!vfull) {
+        u32x4 keep;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          bf16x8 vf = as_bf16x8(vreg[r][db]);
-          if (!vfull) {  // values of keys outside the range must not reach the MFMA
+        for (int jj = 0; jj < 4; ++jj) {
+          uint32_t m = 0u;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int kk = (j < 4) ? 4 * q4 + j : 16 + 4 * q4 + j - 4;
-              const int kpos = pos0 + kk;
-              if (kpos < r_beg || kpos >= r_end) vf[j] = (__bf16)0.f;
-            }
+          for (int h = 0; h < 2; ++h) {
+            const int j = 2 * jj + h;
+            const int kpos = pos0 + ((j < 4) ? 4 * q4 + j : 16 + 4 * q4 + j - 4);
+            if (kpos >= r_beg && kpos < r_end) m |= 0xffffu << (16 * h);
           }
-          oacc[db] = mfma32(vf, pf, oacc[db]);
+          keep[jj] = m;
         }
-        if (has_next) load_v(r, nxt);
-      } else {
-        // the K block doubles as V: each phase stages TRH of its sub-tiles in
-        // this wave's LDS area in operand order; one transposing 64-bit read
-        // per lane then yields V[4q .. 4q+3][d0 + c] for a 16-dim block (the
-        // lane addresses key 4q + c/4, dims d0 + 4(c%4) .. +3).  LDS
-        // operations of one wave complete in order.
 #pragma unroll
-        for (int ph = 0; ph < S::NPH; ++ph) {
+        for (int db = 0; db < NDB; ++db) vreg[r][db] &= keep;
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(as_bf16x8(vreg[r][db]), pf8, oacc[db]);
+      if (PFX) {
+        pin_after(oacc);
+        load_v(r, nxt);
+      }
+    } else {
+      // The K block doubles as V: each phase stages TRH of its sub-tiles in
+      // this wave's LDS area in operand order, after which their registers
+      // take the next block's sub-tiles.  One transposing 64-bit read per
+      // lane then yields V[4q .. 4q+3][d0 + c] for a 16-dim block (the lane
+      // addresses key 4q + c/4, dims d0 + 4(c%4) .. +3).  LDS operations of
+      // one wave complete in order.  In a block that reaches outside
+      // [r_beg, r_end), the staged rows of those keys are overwritten with
+      // zeros (lane L of a sub-tile holds key L % 16).
+      const bool key_out = pos0 + c16 < r_beg || pos0 + c16 >= r_end;
+#pragma unroll
+      for (int ph = 0; ph < S::NPH; ++ph) {
+        if constexpr (!SAG) {
 #pragma unroll
           for (int s = 0; s < S::TRH; ++s)
             *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[r][0][ph * S::TRH + s];
-#pragma unroll
-          for (int dbl = 0; dbl < NDB / S::NPH; ++dbl) {
-            const int dd = 16 * dbl + 4 * (c16 & 3);  // dim within the staged sub-tiles
-            const int kk = 4 * q4 + (c16 >> 2);
-            uint16_t* src = tr + (dd / 32) * 512 + ((dd % 32) / 8) * 128 + kk * 8 + (dd % 8);
-            const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src);
-            bf16x4 vf = __builtin_bit_cast(bf16x4, raw);
-            if (!vfull) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int kpos = pos0 + 4 * q4 + j;
-                if (kpos < r_beg || kpos >= r_end) vf[j] = (__bf16)0.f;
-              }
-            }
-            const int db = ph * (NDB / S::NPH) + dbl;
-            oacc[db] = mfma16(vf, pb[0], oacc[db]);
-          }
         }
-        if (has_next) load_k(r, nxt);
+        if (!SAG && PFX) {
+          asm volatile("" ::: "memory");  // after the staging writes
+#pragma unroll
+          for (int s = 0; s < S::TRH; ++s)
+            kreg[r][0][ph * S::TRH + s] = ldg16(kbn + (ph * S::TRH + s) * 512);
+        }
+        if (!vfull && key_out) {
+#pragma unroll
+          for (int s = 0; s < S::TRH; ++s)
+            *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int dbl = 0; dbl < NDB / S::NPH; ++dbl) {
+          const int dd = 16 * dbl + 4 * (c16 & 3);  // dim within the staged sub-tiles
+          const int kk = 4 * q4 + (c16 >> 2);
+          uint16_t* src = tr + (dd / 32) * 512 + ((dd % 32) / 8) * 128 + kk * 8 + (dd % 8);
+          const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src);
+          const int db = ph * (NDB / S::NPH) + dbl;
+          oacc[db] = mfma16(__builtin_bit_cast(bf16x4, raw), pb[0], oacc[db]);
+        }
       }
     }
+  };
+
+  if (n_mine > 0) {
+    int blk = blk_first + w;
+    if constexpr (PF > 1) {
+      // ring: block i lives in slot i % PF and is replaced by block i + PF
+      for (int i0 = 0; i0 < n_mine; i0 += PF) {
+#pragma unroll
+        for (int r = 0; r < PF; ++r) {
+          const int i = i0 + r;
+          if (i < n_mine) block(blk + i * NW, r, i + PF < n_mine);
+        }
+      }
+    } else if constexpr (KEQV || D >= 512) {
+      // k_eq_v: no older load is waited for after the next block's loads
+      // are issued, so a run-time condition costs nothing.  head_dim 512 with
+      // a V plane: a second copy of the body does not fit the registers.
+      for (int i = 1; i <= n_mine; ++i, blk += NW) block(blk, 0, i < n_mine);
+    } else {
+      for (int i = 1; i < n_mine; ++i, blk += NW) block(blk, 0, std::true_type{});
+      block(blk, 0, std::false_type{});
     }
   }
 
@@ -739,19 +831,22 @@ template <int D, bool KEQV>
 hipError_t decode_launch(const DecodeArgs& a, int batch, hipStream_t s) {
   dim3 grid(a.n_splits, a.n_kv * a.n_hblk, batch);
   PrefillArgs none{};
-  hipLaunchKernelGGL((attend_kernel<D, KEQV, 4, false, decode_prefetch(D, KEQV)>), grid, dim3(256),
-                     0, s, a, none);
+  hipLaunchKernelGGL((attend_kernel<D, KEQV, 4, false, 1>), grid, dim3(256), 0, s, a, none);
   return hipGetLastError();
 }
 
 template <int D, bool KEQV>
 hipError_t prefill_launch(const PrefillArgs& a, hipStream_t s) {
   // eight waves per row block, four where a wave needs all 512 registers
+  // (head_dim 512 with a V plane).  A deeper register ring (PF > 1, one wave
+  // per SIMD) measured slower on every layer type: with a single wave per
+  // SIMD nothing hides its own instruction latencies.
+  constexpr int PF = 1;
   constexpr int NW = (D >= 512 && !KEQV) ? 4 : 8;
   const int n_log = a.n_rowblk * a.n_kv * a.batch;
   dim3 grid(8 * ((n_log + 7) / 8));
   DecodeArgs none{};
-  hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, true, 1>), grid, dim3(NW * 64), 0, s, none, a);
+  hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, true, PF>), grid, dim3(NW * 64), 0, s, none, a);
   return hipGetLastError();
 }
 

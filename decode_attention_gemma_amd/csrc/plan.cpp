@@ -351,9 +351,7 @@ int32_t g4attn_decode(const g4attn_stack* st, int32_t layer, const void* q,
   const int nh = G < 16 ? G : 16;
   const int keys_max = d.window > 0 && d.window < max_seq_len ? d.window : max_seq_len;
   g4::DecodeArgs a;
-  // a decode workgroup has one wave per SIMD
-  const int wgs_per_cu = g4::waves_per_simd(d.head_dim, d.k_eq_v != 0,
-                                            g4::decode_prefetch(d.head_dim, d.k_eq_v != 0));
+  const int wgs_per_cu = g4::waves_per_simd(d.head_dim, d.k_eq_v != 0);
   const int KB = g4::decode_block(d.k_eq_v != 0);
   decode_splits(keys_max, KB, batch * d.n_kv_heads * n_hblk, wgs_per_cu, &a.blocks_per_split,
                 &a.n_splits);
