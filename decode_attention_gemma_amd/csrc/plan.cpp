@@ -85,8 +85,12 @@ int32_t check_layer(const g4attn_stack* st, int32_t layer) {
 // Decode split policy: splits hold a fixed number of key blocks, sized so
 // that a sequence of the longest (hinted) length uses enough splits for the
 // grid to cover every CU `wgs_per_cu` times; shorter sequences use fewer.
-void decode_splits(int keys_max, int KB, int pairs, int wgs_per_cu, int* blocks_per_split,
-                   int* n_splits) {
+// A split also writes rows x head_dim fp32 partial outputs (and reads them
+// back in the merge); splits are made long enough that these stay within
+// an eighth of the split's cache bytes (this binds where many query heads
+// share one KV head, e.g. 16 rows over 16-key k_eq_v blocks).
+void decode_splits(int keys_max, int KB, int pairs, int wgs_per_cu, int rows, int planes,
+                   int* blocks_per_split, int* n_splits) {
   const int nb_max = (keys_max + KB - 1) / KB + 1;  // +1: alignment of the first block
   const int target_wgs = 256 * wgs_per_cu;
   int ns = ceil_div(target_wgs, pairs);
@@ -94,6 +98,10 @@ void decode_splits(int keys_max, int KB, int pairs, int wgs_per_cu, int* blocks_
   if (ns > nb_max) ns = nb_max;
   if (ns < 1) ns = 1;
   int bps = ceil_div(nb_max, ns);
+  // partial bytes per split: rows * D * 4; cache bytes per block: KB * D * 2 * planes
+  const int min_bps = ceil_div(8 * rows * 4, KB * 2 * planes);
+  if (ns > 1 && bps < min_bps) bps = min_bps;
+  if (bps < ceil_div(nb_max, g4::kMaxDecodeSplits)) bps = ceil_div(nb_max, g4::kMaxDecodeSplits);
   *blocks_per_split = bps;
   *n_splits = ceil_div(nb_max, bps);
 }
@@ -353,8 +361,8 @@ int32_t g4attn_decode(const g4attn_stack* st, int32_t layer, const void* q,
   g4::DecodeArgs a;
   const int wgs_per_cu = g4::waves_per_simd(d.head_dim, d.k_eq_v != 0);
   const int KB = g4::decode_block(d.k_eq_v != 0);
-  decode_splits(keys_max, KB, batch * d.n_kv_heads * n_hblk, wgs_per_cu, &a.blocks_per_split,
-                &a.n_splits);
+  decode_splits(keys_max, KB, batch * d.n_kv_heads * n_hblk, wgs_per_cu, nh, d.k_eq_v ? 1 : 2,
+                &a.blocks_per_split, &a.n_splits);
   a.merge_in_kernel =
       (int64_t)a.n_splits * nh * d.head_dim * 4 <= kInKernelMergeBytes ? 1 : 0;
   a.q = static_cast<const uint16_t*>(q);

@@ -417,3 +417,71 @@ def test_graph_replays_match_eager():
         for a, b in zip(bufs.out, eager):
             assert torch.equal(a, b), rep
         _ = torch.randn(1000, device=DEV).sum().item()  # unrelated eager work between replays
+
+
+# ---------------------------------------------------------------------------
+# robustness of the masking and of the online softmax
+# ---------------------------------------------------------------------------
+
+GARBAGE_LAYERS = [
+    # nq, nkv, D, window, keqv
+    (4, 2, 32, 8, 0),
+    (16, 8, 256, 100, 0),
+    (16, 1, 512, 0, 1),
+    (12, 4, 64, 16, 1),
+    (16, 1, 512, 0, 0),
+]
+
+
+@pytest.mark.parametrize("nq,nkv,D,window,keqv", GARBAGE_LAYERS)
+def test_cache_slots_outside_the_visible_range_may_hold_any_bits(nq, nkv, D, window, keqv):
+    """Slots of a key block that no query may see (older than the window,
+    beyond the current length, never written) are filled with all-ones bytes,
+    a NaN pattern in bf16: outputs stay finite and equal to the oracle's, in
+    decode and in prefill."""
+    say(f"[gpu] garbage cache nq={nq} nkv={nkv} D={D} W={window} k_eq_v={keqv}")
+    desc = _desc(nq, nkv, D, window, keqv)
+    lens = [1, 7, 33, 150, 301]
+    wl = _custom([desc], len(lens), "decode", kv_max=512, seq_lens=lens)
+    st = H.make_stack(wl, DEV)
+    st.cache.fill_(255)
+    H.fill_cache(st, wl, DEV)
+    bufs = H.StepBuffers(wl, DEV)
+    H.run_step(st, bufs)
+    torch.cuda.synchronize()
+    q = f64(bufs.q[0])
+    ref = np.stack([oracle_decode(wl, 0, b, q) for b in range(wl.batch)])
+    check_close(bufs.out[0], ref, "decode over garbage cache")
+
+    starts = [0, 21, 130]
+    wp = _custom([desc], len(starts), "prefill", kv_max=512, max_chunk=64, start_pos=starts,
+                 n_tok=40)
+    st = H.make_stack(wp, DEV)
+    st.cache.fill_(255)
+    H.fill_cache(st, wp, DEV)
+    bufs = H.StepBuffers(wp, DEV)
+    H.run_step(st, bufs)
+    torch.cuda.synchronize()
+    q = f64(bufs.q[0])
+    ref = np.stack([oracle_prefill(wp, 0, b, q) for b in range(wp.batch)])
+    check_close(bufs.out[0], ref, "prefill over garbage cache")
+
+
+@pytest.mark.parametrize("D,keqv,window", [(256, 0, 0), (512, 1, 0), (64, 0, 40)])
+def test_peaked_softmax_many_running_max_updates(D, keqv, window):
+    """A large scale makes scores span thousands of units: the running max
+    moves often and by far more than the lazy-rescale margin, and the softmax
+    is close to one-hot.  Decode and prefill stay within tolerance."""
+    say(f"[gpu] peaked softmax D={D} k_eq_v={keqv} W={window}")
+    desc = _desc(16, 4 if not keqv else 1, D, window, keqv, scale=3.0)
+    lens = [2, 90, 513, 1200]
+    wl = _custom([desc], len(lens), "decode", kv_max=2048, seq_lens=lens, seed=5)
+    st, bufs = run_workload(wl)
+    q = f64(bufs.q[0])
+    ref = np.stack([oracle_decode(wl, 0, b, q) for b in range(wl.batch)])
+    check_close(bufs.out[0], ref, "peaked decode")
+    wp = _custom([desc], 2, "prefill", kv_max=2048, start_pos=[0, 700], n_tok=64, seed=6)
+    st, bufs = run_workload(wp)
+    q = f64(bufs.q[0])
+    ref = np.stack([oracle_prefill(wp, 0, b, q) for b in range(wp.batch)])
+    check_close(bufs.out[0], ref, "peaked prefill")
