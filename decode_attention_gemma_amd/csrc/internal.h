@@ -31,12 +31,13 @@ constexpr int kPrefillRows = 16;
 inline int decode_block(bool k_eq_v) { return k_eq_v ? 16 : 32; }
 
 // Waves per SIMD an attention kernel instance is built for: 2 (up to 256
-// registers per lane), or 1 where one wave needs more: head_dim 512 without
-// k_eq_v (its V block and accumulators alone take 256), or a ring of more
-// than one key block in flight.  A decode workgroup has one wave per SIMD, so
-// this is also its workgroups per CU.
-__host__ __device__ constexpr int waves_per_simd(int head_dim, bool k_eq_v, int ring = 1) {
-  return ring > 1 || (head_dim >= 512 && !k_eq_v) ? 1 : 2;
+// registers per lane), or 1 where one wave needs more (head_dim 512 without
+// k_eq_v: its V block and accumulators alone take 256).  A decode workgroup
+// has one wave per SIMD, so this is also its workgroups per CU.  (Deeper
+// per-wave prefetch at one wave per SIMD measured slower on every layer
+// type: with a single wave per SIMD nothing hides its own latencies.)
+__host__ __device__ constexpr int waves_per_simd(int head_dim, bool k_eq_v) {
+  return head_dim >= 512 && !k_eq_v ? 1 : 2;
 }
 
 // Byte offsets of element d of the K row / V row in one segment.

@@ -351,7 +351,7 @@ __global__ __launch_bounds__(D / 4 > 64 ? D / 4 : 64) void merge_kernel(MergeArg
 // results exist.  The grid is laid out so that the row blocks of one
 // (sequence, KV head) run on the same XCD and share its L2.
 
-template <int D, bool KEQV, int NW, int PF, bool SAG>
+template <int D, bool KEQV, int NW, bool SAG>
 struct Shape {
   static constexpr int KB = KEQV ? 16 : 32;  // keys per block
   static constexpr int NSB = KB / 16;        // 16-key score blocks per block
@@ -374,15 +374,15 @@ struct Shape {
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D, bool KEQV, int NW, bool PREFILL, int PF>
-__global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PF)) void attend_kernel(
+template <int D, bool KEQV, int NW, bool PREFILL>
+__global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kernel(
     DecodeArgs da, PrefillArgs pa) {
   // k_eq_v prefill stages each K sub-tile for the V^T transpose as soon as
   // its score MFMA has read it, and reloads the register with the next
   // block's sub-tile at once (a whole block of prefetch distance; the staging
   // area then holds a full block per wave)
   constexpr bool SAG = PREFILL && KEQV;
-  using S = Shape<D, KEQV, NW, PF, SAG>;
+  using S = Shape<D, KEQV, NW, SAG>;
   constexpr int KB = S::KB, NSB = S::NSB, KS = S::KS, NDB = S::NDB;
   constexpr int D4 = D / 4;
   constexpr int NT = NW * 64;
@@ -487,37 +487,35 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PF)) void attend_k
   // compiler wait for exactly the loads an instruction needs (memory counters
   // complete in issue order; after a conditional prefetch of the next K, the
   // wait for the current V would also cover the first of those loads) ----
-  u32x4 kreg[PF][NSB][KS];  // PF > 1: a ring of blocks blk, blk + NW, ...
-  u32x4 vreg[PF][KEQV ? 1 : NDB];
+  u32x4 kreg[NSB][KS];
+  u32x4 vreg[KEQV ? 1 : NDB];
   // this lane's address in the K sub-tile 0 of a block (sub-tile s of score
   // block sb follows at (sb * KS + s) * 512 elements)
   auto kblock = [&](int blk) {
     const int slot0 = (blk * KB) % cap;
     return kseg + (size_t)(slot0 / 16) * KS * 512 + lane * 8;
   };
-  auto load_k = [&](int r, int blk) {
+  auto load_k = [&](int blk) {
     const uint16_t* kb = kblock(blk);
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kreg[r][sb][s] = ldg16(kb + (sb * KS + s) * 512);
+      for (int s = 0; s < KS; ++s) kreg[sb][s] = ldg16(kb + (sb * KS + s) * 512);
   };
-  auto load_v = [&](int r, int blk) {
+  auto load_v = [&](int blk) {
     if constexpr (!KEQV) {
       const int slot0 = (blk * KB) % cap;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        vreg[r][db] = ldg16(vseg + ((size_t)(slot0 / 32) * NDB + db) * 512 + lane * 8);
+        vreg[db] = ldg16(vseg + ((size_t)(slot0 / 32) * NDB + db) * 512 + lane * 8);
     }
   };
   const int n_mine = n_keys > 0 && blk_first + w < blk_end
                          ? (blk_end - (blk_first + w) + NW - 1) / NW : 0;  // blocks of this wave
-#pragma unroll
-  for (int r = 0; r < PF; ++r)
-    if (r < n_mine) {
-      load_k(r, blk_first + w + r * NW);
-      load_v(r, blk_first + w + r * NW);
-    }
+  if (n_mine > 0) {
+    load_k(blk_first + w);
+    load_v(blk_first + w);
+  }
 
   // queries as the B operand of S^T = K Q^T (column c16 = row, k-slots =
   // dims), kept in LDS in operand order: sub-tile s, lane L at (s*64 + L)*8
@@ -533,12 +531,11 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PF)) void attend_k
   float l_run = 0.f;
   uint16_t* tr = reinterpret_cast<uint16_t*>(lds) + w * S::TR_ELEMS;  // k_eq_v only
 
-  // one key block, held in ring slot r; `pf` (a bool, or std::true_type /
-  // std::false_type) says whether the slot's next block (blk + NW * PF) is
-  // loaded
-  auto block = [&](const int blk, const int r, auto pf) {
+  // one key block; `pf` (a bool, or std::true_type / std::false_type) says
+  // whether the wave's next block (blk + NW) is loaded
+  auto block = [&](const int blk, auto pf) {
     const bool PFX = pf;  // a compile-time constant where the caller passes a type
-    const int nxt = blk + NW * PF;
+    const int nxt = blk + NW;
     // the next block's address, computed before any compiler barrier below
     // (those make captured values be reloaded)
     const uint16_t* const kbn = kblock(nxt);
@@ -565,12 +562,12 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PF)) void attend_k
         const bf16x8 qf = *reinterpret_cast<const bf16x8*>(&Qs[(s * 64 + lane) * 8]);
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb)
-          sch[sb][s % NCH] = mfma32(as_bf16x8(kreg[r][sb][s]), qf, sch[sb][s % NCH]);
+          sch[sb][s % NCH] = mfma32(as_bf16x8(kreg[sb][s]), qf, sch[sb][s % NCH]);
         if constexpr (SAG) {
-          *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[r][0][s];
+          *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[0][s];
           if (PFX) {
             asm volatile("" ::: "memory");  // after the staging write
-            kreg[r][0][s] = ldg16(kbn + s * 512);
+            kreg[0][s] = ldg16(kbn + s * 512);
           }
         }
       }
@@ -585,7 +582,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PF)) void attend_k
       // the next K lands in the registers the score MFMAs just read: keep
       // its loads after them (hoisting them would need a second set)
       pin_after(sacc);
-      load_k(r, nxt);
+      load_k(nxt);
     }
     // visible keys of this lane's row within the block (bitwise, no branches)
     const int vis_lo = full ? INT_MIN : row_lo;
@@ -656,13 +653,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PF)) void attend_k
           keep[jj] = m;
         }
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) vreg[r][db] &= keep;
+        for (int db = 0; db < NDB; ++db) vreg[db] &= keep;
       }
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(as_bf16x8(vreg[r][db]), pf8, oacc[db]);
+      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(as_bf16x8(vreg[db]), pf8, oacc[db]);
       if (PFX) {
         pin_after(oacc);
-        load_v(r, nxt);
+        load_v(nxt);
       }
     } else {
       // The K block doubles as V: each phase stages TRH of its sub-tiles in
@@ -679,13 +676,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PF)) void attend_k
         if constexpr (!SAG) {
 #pragma unroll
           for (int s = 0; s < S::TRH; ++s)
-            *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[r][0][ph * S::TRH + s];
+            *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[0][ph * S::TRH + s];
         }
         if (!SAG && PFX) {
           asm volatile("" ::: "memory");  // after the staging writes
 #pragma unroll
           for (int s = 0; s < S::TRH; ++s)
-            kreg[r][0][ph * S::TRH + s] = ldg16(kbn + (ph * S::TRH + s) * 512);
+            kreg[0][ph * S::TRH + s] = ldg16(kbn + (ph * S::TRH + s) * 512);
         }
         if (!vfull && key_out) {
 #pragma unroll
@@ -707,23 +704,14 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PF)) void attend_k
 
   if (n_mine > 0) {
     int blk = blk_first + w;
-    if constexpr (PF > 1) {
-      // ring: block i lives in slot i % PF and is replaced by block i + PF
-      for (int i0 = 0; i0 < n_mine; i0 += PF) {
-#pragma unroll
-        for (int r = 0; r < PF; ++r) {
-          const int i = i0 + r;
-          if (i < n_mine) block(blk + i * NW, r, i + PF < n_mine);
-        }
-      }
-    } else if constexpr (KEQV || D >= 512) {
+    if constexpr (KEQV || D >= 512) {
       // k_eq_v: no older load is waited for after the next block's loads
       // are issued, so a run-time condition costs nothing.  head_dim 512 with
       // a V plane: a second copy of the body does not fit the registers.
-      for (int i = 1; i <= n_mine; ++i, blk += NW) block(blk, 0, i < n_mine);
+      for (int i = 1; i <= n_mine; ++i, blk += NW) block(blk, i < n_mine);
     } else {
-      for (int i = 1; i < n_mine; ++i, blk += NW) block(blk, 0, std::true_type{});
-      block(blk, 0, std::false_type{});
+      for (int i = 1; i < n_mine; ++i, blk += NW) block(blk, std::true_type{});
+      block(blk, std::false_type{});
     }
   }
 
@@ -831,22 +819,19 @@ template <int D, bool KEQV>
 hipError_t decode_launch(const DecodeArgs& a, int batch, hipStream_t s) {
   dim3 grid(a.n_splits, a.n_kv * a.n_hblk, batch);
   PrefillArgs none{};
-  hipLaunchKernelGGL((attend_kernel<D, KEQV, 4, false, 1>), grid, dim3(256), 0, s, a, none);
+  hipLaunchKernelGGL((attend_kernel<D, KEQV, 4, false>), grid, dim3(256), 0, s, a, none);
   return hipGetLastError();
 }
 
 template <int D, bool KEQV>
 hipError_t prefill_launch(const PrefillArgs& a, hipStream_t s) {
   // eight waves per row block, four where a wave needs all 512 registers
-  // (head_dim 512 with a V plane).  A deeper register ring (PF > 1, one wave
-  // per SIMD) measured slower on every layer type: with a single wave per
-  // SIMD nothing hides its own instruction latencies.
-  constexpr int PF = 1;
+  // (head_dim 512 with a V plane)
   constexpr int NW = (D >= 512 && !KEQV) ? 4 : 8;
   const int n_log = a.n_rowblk * a.n_kv * a.batch;
   dim3 grid(8 * ((n_log + 7) / 8));
   DecodeArgs none{};
-  hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, true, PF>), grid, dim3(NW * 64), 0, s, none, a);
+  hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, true>), grid, dim3(NW * 64), 0, s, none, a);
   return hipGetLastError();
 }
 
