@@ -351,7 +351,7 @@ __global__ __launch_bounds__(D / 4 > 64 ? D / 4 : 64) void merge_kernel(MergeArg
 // results exist.  The grid is laid out so that the row blocks of one
 // (sequence, KV head) run on the same XCD and share its L2.
 
-template <int D, bool KEQV, int NW, bool SAG>
+template <int D, bool KEQV, int NW, bool SAG, bool PREFILL>
 struct Shape {
   static constexpr int KB = KEQV ? 16 : 32;  // keys per block
   static constexpr int NSB = KB / 16;        // 16-key score blocks per block
@@ -365,11 +365,22 @@ struct Shape {
   // cross-wave reduction rows are padded by 4 floats so that the 16 rows a
   // wave writes at once start on different LDS banks
   static constexpr int RED_STRIDE = D + 4;
-  static constexpr int RED_BYTES = 16 * RED_STRIDE * 4;
+  static constexpr int SLOT_BYTES = 16 * RED_STRIDE * 4;
   static constexpr int MERGE_BYTES = (2 * 16 * kMaxDecodeSplits + 16) * 4;
   static constexpr int TR_BYTES = NW * TR_ELEMS * 2;
-  static constexpr int A_BYTES = TR_BYTES > RED_BYTES ? TR_BYTES : RED_BYTES;
-  static constexpr int LDS_BYTES = A_BYTES > MERGE_BYTES ? A_BYTES : MERGE_BYTES;
+  static constexpr int Q_BYTES = KS * 512 * 2;
+  // The waves combine their partial outputs in NSL reduction slots: one per
+  // wave (one barrier), one per pair of waves (two), or a single slot that
+  // the waves add into one after another.  Slots share the LDS with the
+  // transpose area; a decode workgroup stays within what lets two of them
+  // share a CU, a prefill workgroup (one per CU) may use most of it.
+  static constexpr int BUDGET = PREFILL ? 150 * 1024 : 78 * 1024;
+  static constexpr int cmax(int a, int b) { return a > b ? a : b; }
+  static constexpr bool fits(int n) {
+    return cmax(cmax(TR_BYTES, n * SLOT_BYTES), MERGE_BYTES) + Q_BYTES + 1024 <= BUDGET;
+  }
+  static constexpr int NSL = fits(NW) ? NW : (NW % 2 == 0 && fits(NW / 2)) ? NW / 2 : 1;
+  static constexpr int LDS_BYTES = cmax(cmax(TR_BYTES, NSL * SLOT_BYTES), MERGE_BYTES);
 };
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -382,7 +393,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
   // block's sub-tile at once (a whole block of prefetch distance; the staging
   // area then holds a full block per wave)
   constexpr bool SAG = PREFILL && KEQV;
-  using S = Shape<D, KEQV, NW, SAG>;
+  using S = Shape<D, KEQV, NW, SAG, PREFILL>;
   constexpr int KB = S::KB, NSB = S::NSB, KS = S::KS, NDB = S::NDB;
   constexpr int D4 = D / 4;
   constexpr int NT = NW * 64;
@@ -737,27 +748,49 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
   }
   const float mine = fast_exp2(m_run - M_use);
   constexpr int RS = S::RED_STRIDE;
-  float* red = reinterpret_cast<float*>(lds);  // [16][RS]
-  for (int step = NW - 1; step >= 0; --step) {
-    if (w == step && c16 < nrows) {
+  constexpr int NSL = S::NSL;
+  constexpr int SLOT = 16 * RS;                // floats per slot
+  float* red = reinterpret_cast<float*>(lds);  // [NSL][16][RS]
+  auto put = [&](int slot, bool add) {         // this wave's rescaled O into a slot
+    if (c16 < nrows) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        float* p = red + c16 * RS + 16 * db + 4 * q4;
+        float* p = red + slot * SLOT + c16 * RS + 16 * db + 4 * q4;
         f32x4 v = oacc[db] * mine;
-        if (step != NW - 1) v += *reinterpret_cast<f32x4*>(p);
+        if (add) v += *reinterpret_cast<f32x4*>(p);
         *reinterpret_cast<f32x4*>(p) = v;
       }
     }
+  };
+  if constexpr (NSL == NW) {
+    put(w, false);
     __syncthreads();
+  } else if constexpr (2 * NSL == NW) {
+    if (w >= NSL) put(w - NSL, false);
+    __syncthreads();
+    if (w < NSL) put(w, true);
+    __syncthreads();
+  } else {
+    for (int step = NW - 1; step >= 0; --step) {
+      if (w == step) put(0, step != NW - 1);
+      __syncthreads();
+    }
   }
+  // unnormalised O of this key range: row r, dims d .. d+3
+  auto red_sum = [&](int r, int d) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(red + r * RS + d);
+#pragma unroll
+    for (int s = 1; s < NSL; ++s) v += *reinterpret_cast<const f32x4*>(red + s * SLOT + r * RS + d);
+    return v;
+  };
 
-  // red[r][:] = unnormalised O of this key range for row r; hM, hL per row
+  // red_sum(r, .) = unnormalised O of this key range for row r; hM, hL per row
   if (PREFILL || n_used <= 1) {
     for (int idx = tid; idx < nrows * D4; idx += NT) {
       const int r = idx / D4;
       const int d = 4 * (idx - r * D4);
       const float il = hL[r] > 0.f ? 1.f / hL[r] : 0.f;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(red + r * RS + d);
+      const f32x4 v = red_sum(r, d);
       bf16x4 o;
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j] = (__bf16)(v[j] * il);
@@ -781,7 +814,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
     for (int idx = tid; idx < nrows * D4; idx += NT) {
       const int h = idx / D4;
       const int d = 4 * (idx - h * D4);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(red + h * RS + d);
+      const f32x4 v = red_sum(h, d);
       float* dst = a.part_o + (prow0 + (size_t)h * a.n_splits) * D + d;
       if (a.merge_in_kernel)
         st16_coherent(dst, v);
