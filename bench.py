@@ -9,6 +9,7 @@ only on layers that have a V plane) divided by the step time, in GB/s.
 Also reported on the same line:
   roofline      the dominant kernel (sliding-layer decode, head_dim 256),
                 timed over a graph of the 40 sliding-layer launches;
+  tp2_rank_decode  one tensor-parallel rank (TP=2) of the same decode stack;
   prefill       the 12B-shaped 64-token prefill chunk stack (B = 4) after
                 960 and 4032 cached tokens, in TFLOP/s of visible-pair work;
   cpu_baseline  the fp64 oracle on a bounded sample of the same decode
@@ -156,6 +157,29 @@ def bench_decode(args, stream):
     return out
 
 
+def bench_rank_decode(args, stream):
+    """One tensor-parallel rank (TP=2) of the 12B decode stack, whole step."""
+    import torch
+
+    from decode_attention_gemma_amd import harness as H, workloads as W
+
+    wl = W.g12b_tp2_rank_decode()
+    log(f"[bench] setup {wl.name}")
+    st = H.make_stack(wl, "cuda")
+    H.fill_cache(st, wl, "cuda")
+    bufs = H.StepBuffers(wl, "cuda")
+    g = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream), stream)
+    ms = time_graph(g, args.warmup, args.steps)
+    step_bytes = sum(kv_bytes(wl, i) for i in range(wl.n_layers))
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    log(f"[bench] TP=2 rank decode step {ms*1e3:.1f} us, {gbs:.0f} GB/s")
+    del st, bufs, g
+    torch.cuda.empty_cache()
+    return {"workload": wl.name + " (sliding 8q/4kv, global 8q/1kv replicated)",
+            "us_per_step": round(ms * 1e3, 2), "kv_bytes_per_step": step_bytes,
+            "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def bench_prefill(prefix, args, stream):
     import torch
 
@@ -265,6 +289,7 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     dec = bench_decode(args, stream)
+    rank = bench_rank_decode(args, stream)
     prefill = {}
     if not args.no_prefill:
         for p in (960, 4032):
@@ -305,6 +330,7 @@ def main():
             "us_per_launch": round(dom["ms"] * 1e3, 2),
             "bytes_per_launch": dom["bytes"],
         },
+        "tp2_rank_decode": rank,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

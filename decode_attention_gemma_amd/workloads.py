@@ -153,9 +153,46 @@ def long_decode() -> Workload:
                     outlier_mult=8.0)
 
 
+def tp_rank_layers(layers: list, tp: int) -> list:
+    """One tensor-parallel rank's share of a layer stack ("Porting Gemma-4 (2B /
+    4B / 12B) to AWS Inferentia2", 2.2: KV heads are split across ranks when
+    they divide evenly, so each rank keeps whole query-head groups; "Gemma-4
+    12B on AWS Inferentia2 -- Tensor-Parallel (TP=2), device prefill", "The
+    recipe": a layer with fewer KV heads than ranks keeps its one KV head on
+    both ranks and splits only the query heads).  With fewer KV heads than
+    ranks in general, each KV head sits on tp / n_kv ranks and a rank holds
+    one KV head and the query heads that read it."""
+    out = []
+    for d in layers:
+        if d.n_q_heads % tp:
+            raise ValueError(f"{d.n_q_heads} query heads do not split over {tp} ranks")
+        if d.n_kv_heads % tp == 0:
+            out.append(replace(d, n_q_heads=d.n_q_heads // tp, n_kv_heads=d.n_kv_heads // tp))
+        elif tp % d.n_kv_heads == 0:
+            out.append(replace(d, n_q_heads=d.n_q_heads // tp, n_kv_heads=1))
+        else:
+            raise ValueError(f"{d.n_kv_heads} KV heads and {tp} ranks do not divide")
+    return out
+
+
+def g12b_tp2_rank_decode() -> Workload:
+    """One rank of the 12B decode stack at TP=2: sliding 8q/4kv, global 8q/1kv
+    (the KV head replicated, G=8); same batch and lengths as the 12B stack."""
+    wl = g12b_decode()
+    return Workload("12B TP=2 rank 48-layer decode stack", 6, tp_rank_layers(wl.layers, 2),
+                    batch=16, kind="decode", kv_max=4096, seq_lens=list(wl.seq_lens))
+
+
+def e4b_tp2_rank_decode() -> Workload:
+    """One rank of the E4B decode stack at TP=2: 4q/1kv, sharing as in E4B."""
+    return Workload("E4B TP=2 rank 12-layer decode stack", 7,
+                    tp_rank_layers(e4b_decode().layers, 2), batch=1, kind="decode",
+                    kv_max=512, seq_lens=[511])
+
+
 def all_workloads() -> list:
     return [tiny_stack(), e4b_decode(), g12b_decode(), g12b_prefill(0), g12b_prefill(960),
-            g12b_prefill(4032), long_decode()]
+            g12b_prefill(4032), long_decode(), g12b_tp2_rank_decode(), e4b_tp2_rank_decode()]
 
 
 # ----------------------------------------------------------------------------

@@ -175,6 +175,24 @@ def test_long_context_ragged_sampled():
         say(f"  layer {layer} (seqs {bs}, lens {lens[bs].tolist()}): max_abs {m:.2e} rel {r:.2e}")
 
 
+def test_tp2_rank_stacks_sampled():
+    """One tensor-parallel rank of the 12B (sliding 8q/4kv, global 8q/1kv
+    replicated, G=8) and of the E4B (4q/1kv, KV-shared) stacks."""
+    wl = W.g12b_tp2_rank_decode()
+    st, bufs = run_workload(wl)
+    for layer in (0, 5, 47):
+        q = f64(bufs.q[layer])
+        ref = np.stack([oracle_decode(wl, layer, b, q) for b in range(wl.batch)])
+        m, r = check_close(bufs.out[layer], ref, f"12b rank layer {layer}")
+        say(f"  layer {layer}: max_abs {m:.2e} rel {r:.2e}")
+    wl = W.e4b_tp2_rank_decode()
+    st, bufs = run_workload(wl)
+    for layer in range(wl.n_layers):
+        q = f64(bufs.q[layer])
+        ref = np.stack([oracle_decode(wl, layer, b, q) for b in range(wl.batch)])
+        check_close(bufs.out[layer], ref, f"e4b rank layer {layer}")
+
+
 # ---------------------------------------------------------------------------
 # grids of shapes: several tiles, ragged tails, every descriptor branch
 # ---------------------------------------------------------------------------
