@@ -9,6 +9,8 @@ only on layers that have a V plane) divided by the step time, in GB/s.
 Also reported on the same line:
   roofline      the dominant kernel (sliding-layer decode, head_dim 256),
                 timed over a graph of the 40 sliding-layer launches;
+  decode_step_with_append  the same step including the current token's
+                K/V write: append + decode per layer vs the fused call;
   tp2_rank_decode  one tensor-parallel rank (TP=2) of the same decode stack;
   prefill       the 12B-shaped 64-token prefill chunk stack (B = 4) after
                 960 and 4032 cached tokens, in TFLOP/s of visible-pair work;
@@ -157,6 +159,51 @@ def bench_decode(args, stream):
     return out
 
 
+def bench_fused_step(args, stream):
+    """The 12B decode step including the current token's K/V write, as a
+    separate g4attn_append_kv + g4attn_decode per layer and as one fused
+    g4attn_decode_append per layer."""
+    import torch
+
+    from decode_attention_gemma_amd import harness as H, workloads as W
+
+    wl = W.g12b_decode()
+    log(f"[bench] setup {wl.name} (with the token append)")
+    st = H.make_stack(wl, "cuda")
+    H.fill_cache(st, wl, "cuda")
+    bufs = H.StepBuffers(wl, "cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4321)
+    knew, vnew = [], []
+    for d in wl.layers:
+        shape = (wl.batch, d.n_kv_heads, d.head_dim)
+        knew.append(torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16))
+        vnew.append(None if d.k_eq_v else
+                    torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16))
+    pos = (bufs.lens - 1).to(torch.int32)
+    sid = stream.cuda_stream
+
+    def separate():
+        for i in range(wl.n_layers):
+            st.append_kv(i, knew[i][:, None], None if vnew[i] is None else vnew[i][:, None], pos,
+                         max_end_pos=bufs.max_len, stream=sid)
+            st.decode(i, bufs.q[i], bufs.lens, bufs.max_len, bufs.out[i], sid)
+
+    def fused():
+        for i in range(wl.n_layers):
+            st.decode_append(i, bufs.q[i], knew[i], vnew[i], bufs.lens, bufs.max_len, bufs.out[i],
+                             sid)
+
+    ms_sep = time_graph(graph_of(separate, stream), args.warmup, args.steps)
+    ms_fus = time_graph(graph_of(fused, stream), args.warmup, args.steps)
+    log(f"[bench] decode step with token append: separate {ms_sep*1e3:.1f} us, "
+        f"fused {ms_fus*1e3:.1f} us")
+    del st, bufs
+    torch.cuda.empty_cache()
+    return {"separate_append_then_decode_us": round(ms_sep * 1e3, 2),
+            "fused_decode_append_us": round(ms_fus * 1e3, 2)}
+
+
 def bench_rank_decode(args, stream):
     """One tensor-parallel rank (TP=2) of the 12B decode stack, whole step."""
     import torch
@@ -290,6 +337,7 @@ def main():
         torch.cuda.empty_cache()
     dec = bench_decode(args, stream)
     rank = bench_rank_decode(args, stream)
+    fused = bench_fused_step(args, stream)
     prefill = {}
     if not args.no_prefill:
         for p in (960, 4032):
@@ -330,6 +378,7 @@ def main():
             "us_per_launch": round(dom["ms"] * 1e3, 2),
             "bytes_per_launch": dom["bytes"],
         },
+        "decode_step_with_append": fused,
         "tp2_rank_decode": rank,
         "prefill": prefill,
         "cpu_baseline": cpu,

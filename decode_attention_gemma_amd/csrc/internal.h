@@ -65,8 +65,13 @@ struct AppendArgs {
 
 struct DecodeArgs {
   const uint16_t* q;  // [B][n_q][D]
-  const uint16_t* kp;
-  const uint16_t* vp;  // == kp when k_eq_v
+  uint16_t* kp;       // written only when k_new is set
+  uint16_t* vp;       // == kp when k_eq_v
+  // Optional: the current token's K (and V) rows [B][n_kv][D], written into
+  // the cache at position seq_lens[b] - 1 before it is attended (nullptr:
+  // the token is already in the cache)
+  const uint16_t* k_new;
+  const uint16_t* v_new;  // nullptr when k_eq_v
   const int32_t* seq_lens;
   uint16_t* out;     // [B][n_q][D]
   float* part_o;     // [B][n_q][n_splits][D]

@@ -421,6 +421,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
   float scale_log2;
   // decode only
   int split = 0, n_used = 1, head0 = 0, hblk = 0;
+  int new_pos = -1;  // fused append: position of the current token in this split
   // prefill only
   int row0 = 0, t_row = 0, h_row = 0;
   if constexpr (!PREFILL) {
@@ -447,6 +448,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
     row_hi = r_end;
     row_ok = c16 < nrows;
     qrow = a.q + ((size_t)b * a.n_q + head0 + c16) * D;
+    if (a.k_new != nullptr && L > 0 && r_end == L) new_pos = L - 1;
   } else {
     const PrefillArgs& a = pa;
     // physical workgroup p runs on XCD p % 8; give each XCD a contiguous
@@ -523,6 +525,26 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
   };
   const int n_mine = n_keys > 0 && blk_first + w < blk_end
                          ? (blk_end - (blk_first + w) + NW - 1) / NW : 0;  // blocks of this wave
+  if constexpr (!PREFILL) {
+    // Fused append: the wave that will read the current token's block writes
+    // the token's K (and V) row into its cache slot and waits for the stores
+    // before loading anything, so its loads see the row.  No other workgroup
+    // of this launch reads that slot as a visible key.  (Several head blocks
+    // of one KV head write the same bytes.)
+    if (new_pos >= 0 && w == (new_pos / KB - blk_first) % NW) {
+      const int slot = new_pos % cap;
+      const size_t row = ((size_t)b * n_kv + g) * D;
+      uint16_t* kdst = da.kp + seg;
+      for (int c = lane; c < D / 8; c += 64)
+        *reinterpret_cast<u32x4*>(kdst + k_elem_offset(slot, 8 * c, D) / 2) =
+            ldg16(da.k_new + row + 8 * c);
+      if constexpr (!KEQV) {
+        uint16_t* vdst = da.vp + seg;
+        for (int d = lane; d < D; d += 64) vdst[v_elem_offset(slot, d, D) / 2] = da.v_new[row + d];
+      }
+      wait_vmem();
+    }
+  }
   if (n_mine > 0) {
     load_k(blk_first + w);
     load_v(blk_first + w);

@@ -339,10 +339,14 @@ int32_t g4attn_append_kv(const g4attn_stack* st, int32_t layer, const void* k, c
   return ok();
 }
 
-int32_t g4attn_decode(const g4attn_stack* st, int32_t layer, const void* q,
-                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, void* out,
-                      void* stream) {
-  if (int32_t rc = check_layer(st, layer)) return rc;
+}  // extern "C"
+
+namespace {
+
+// Decode, optionally writing the current token's K / V rows first (k_new).
+int32_t decode_impl(const g4attn_stack* st, int32_t layer, const void* q, const void* k_new,
+                    const void* v_new, const int32_t* seq_lens, int32_t batch,
+                    int32_t max_seq_len, void* out, void* stream) {
   if (!q || !seq_lens || !out) return fail(G4ATTN_ERR_NULL, "q, seq_lens and out must be non-NULL");
   if (batch <= 0 || batch > st->max_batch)
     return fail(G4ATTN_ERR_RANGE, "batch %d not in [1, %d]", batch, st->max_batch);
@@ -366,8 +370,10 @@ int32_t g4attn_decode(const g4attn_stack* st, int32_t layer, const void* q,
   a.merge_in_kernel =
       (int64_t)a.n_splits * nh * d.head_dim * 4 <= kInKernelMergeBytes ? 1 : 0;
   a.q = static_cast<const uint16_t*>(q);
-  a.kp = reinterpret_cast<const uint16_t*>(st->cache + p.k_off);
-  a.vp = reinterpret_cast<const uint16_t*>(st->cache + p.v_off);
+  a.kp = reinterpret_cast<uint16_t*>(st->cache + p.k_off);
+  a.vp = reinterpret_cast<uint16_t*>(st->cache + p.v_off);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
   a.seq_lens = seq_lens;
   a.out = static_cast<uint16_t*>(out);
   a.counters = reinterpret_cast<int32_t*>(st->ws + st->ws_ctr_off);
@@ -401,6 +407,31 @@ int32_t g4attn_decode(const g4attn_stack* st, int32_t layer, const void* q,
   }
   if (e != hipSuccess) return fail(G4ATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t g4attn_decode(const g4attn_stack* st, int32_t layer, const void* q,
+                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, void* out,
+                      void* stream) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  return decode_impl(st, layer, q, nullptr, nullptr, seq_lens, batch, max_seq_len, out, stream);
+}
+
+int32_t g4attn_decode_append(const g4attn_stack* st, int32_t layer, const void* q,
+                             const void* k_new, const void* v_new, const int32_t* seq_lens,
+                             int32_t batch, int32_t max_seq_len, void* out, void* stream) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  const LayerPlan& p = st->L[layer];
+  if (p.owner != layer)
+    return fail(G4ATTN_ERR_SHARED_LAYER, "layer %d reads layer %d's cache and writes none", layer,
+                p.owner);
+  if (!k_new) return fail(G4ATTN_ERR_NULL, "k_new must be non-NULL");
+  if (p.d.k_eq_v && v_new) return fail(G4ATTN_ERR_NULL, "v_new must be NULL on a k_eq_v layer");
+  if (!p.d.k_eq_v && !v_new) return fail(G4ATTN_ERR_NULL, "v_new must be non-NULL");
+  return decode_impl(st, layer, q, k_new, v_new, seq_lens, batch, max_seq_len, out, stream);
 }
 
 int32_t g4attn_prefill(const g4attn_stack* st, int32_t layer, const void* q,

@@ -59,6 +59,8 @@ _SIGNATURES = {
                                    c_int32, c_int32, c_int32, c_void_p]),
     "g4attn_decode": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32,
                                 c_void_p, c_void_p]),
+    "g4attn_decode_append": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "g4attn_prefill": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32,
                                  c_int32, c_void_p, c_void_p]),
     "g4attn_last_error": (ctypes.c_char_p, []),
@@ -209,6 +211,13 @@ def g4attn_decode(stack: int, layer: int, q, seq_lens, batch: int, max_seq_len: 
                                 _ptr(out), _stream(stream)))
 
 
+def g4attn_decode_append(stack: int, layer: int, q, k_new, v_new, seq_lens, batch: int,
+                         max_seq_len: int, out, stream=None) -> None:
+    _check(load().g4attn_decode_append(stack, layer, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                       _ptr(seq_lens), batch, max_seq_len, _ptr(out),
+                                       _stream(stream)))
+
+
 def g4attn_prefill(stack: int, layer: int, q, start_pos, batch: int, n_tok: int,
                    max_start_pos: int, out, stream=None) -> None:
     _check(load().g4attn_prefill(stack, layer, _ptr(q), _ptr(start_pos), batch, n_tok,
@@ -287,6 +296,27 @@ class Stack:
             out = torch.empty_like(q)
         _expect(out, tuple(q.shape), torch.bfloat16, "out")
         g4attn_decode(self.handle, layer, q, seq_lens, B, max_seq_len, out, stream)
+        return out
+
+    def decode_append(self, layer, q, k_new, v_new, seq_lens, max_seq_len, out=None,
+                      stream=None):
+        """Decode with the current token's K/V written first. q: bf16 [B, n_q, D];
+        k_new, v_new: bf16 [B, n_kv, D] (v_new None on k_eq_v layers);
+        seq_lens: int32 [B] (keys incl. the current one)."""
+        import torch
+
+        d = self.layers[layer]
+        B = q.shape[0]
+        _expect(q, (B, d.n_q_heads, d.head_dim), torch.bfloat16, "q")
+        _expect(k_new, (B, d.n_kv_heads, d.head_dim), torch.bfloat16, "k_new")
+        if v_new is not None:
+            _expect(v_new, (B, d.n_kv_heads, d.head_dim), torch.bfloat16, "v_new")
+        _expect(seq_lens, (B,), torch.int32, "seq_lens")
+        if out is None:
+            out = torch.empty_like(q)
+        _expect(out, tuple(q.shape), torch.bfloat16, "out")
+        g4attn_decode_append(self.handle, layer, q, k_new, v_new, seq_lens, B, max_seq_len, out,
+                             stream)
         return out
 
     def prefill(self, layer, q, start_pos, max_start_pos, out=None, stream=None):

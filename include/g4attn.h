@@ -166,6 +166,24 @@ int32_t g4attn_decode(const g4attn_stack* stack, int32_t layer, const void* q,
                       void* stream);
 
 /*
+ * Decode step with the current token's K/V write fused in ([FR] 4 and 5: the
+ * decode graph writes the new token's K/V into the resident cache in place
+ * and attends over it).  Same as g4attn_append_kv of one token at position
+ * seq_lens[b] - 1 followed by g4attn_decode, in one launch, with bit-identical
+ * results and cache contents.
+ *   k_new: [batch][n_kv_heads][head_dim] bf16, the current token's K rows.
+ *   v_new: same shape, or NULL on a k_eq_v layer (and non-NULL otherwise).
+ *   q, seq_lens, max_seq_len, out: as for g4attn_decode; seq_lens[b] counts
+ *        the current token, whose row is written at position seq_lens[b] - 1
+ *        (nothing is written for a length <= 0).
+ * Errors: _NULL, _RANGE, _SHARED_LAYER (the layer reads another layer's
+ * cache), _UNBOUND, _HIP.
+ */
+int32_t g4attn_decode_append(const g4attn_stack* stack, int32_t layer, const void* q,
+                             const void* k_new, const void* v_new, const int32_t* seq_lens,
+                             int32_t batch, int32_t max_seq_len, void* out, void* stream);
+
+/*
  * Prefill of a chunk of n_tok new tokens per sequence ([12B] "The recipe":
  * the 64-token prefill bucket; causal with the layer's window).
  *   q:   [batch][n_tok][n_q_heads][head_dim] bf16.

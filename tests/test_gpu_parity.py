@@ -503,3 +503,53 @@ def test_peaked_softmax_many_running_max_updates(D, keqv, window):
     q = f64(bufs.q[0])
     ref = np.stack([oracle_prefill(wp, 0, b, q) for b in range(wp.batch)])
     check_close(bufs.out[0], ref, "peaked prefill")
+
+
+# ---------------------------------------------------------------------------
+# fused decode step: append of the current token + decode in one launch
+# ---------------------------------------------------------------------------
+
+FUSED_GRID = [
+    # nq, nkv, D, window, keqv, lens, kv_max, max_chunk
+    (16, 8, 256, 100, 0, [1, 33, 64, 129, 400], 512, 64),
+    (16, 1, 512, 0, 1, [1, 16, 17, 700, 2049], 4096, 64),
+    (12, 4, 64, 16, 1, [1, 16, 40, 95], 256, 16),
+    (4, 2, 64, 8, 0, [1, 8, 64, 65, 200], 256, 16),   # ring of 64 slots wraps
+    (32, 1, 64, 0, 0, [3, 200, 513], 1024, 64),         # two head blocks
+]
+
+
+@pytest.mark.parametrize("nq,nkv,D,window,keqv,lens,kv_max,max_chunk", FUSED_GRID)
+def test_fused_decode_step_equals_append_then_decode(nq, nkv, D, window, keqv, lens, kv_max,
+                                                     max_chunk):
+    """g4attn_decode_append == g4attn_append_kv of the token + g4attn_decode:
+    outputs and the whole cache bit-identical; outputs match the oracle."""
+    say(f"[gpu] fused decode nq={nq} nkv={nkv} D={D} W={window} k_eq_v={keqv} lens={lens}")
+    desc = _desc(nq, nkv, D, window, keqv)
+    wl = _custom([desc], len(lens), "decode", kv_max=kv_max, max_chunk=max_chunk, seq_lens=lens)
+    B = wl.batch
+    spans = [W.kv_span(wl, 0, b) for b in range(B)]
+    ks = [W.kv_rows(wl, 0, b, "k", DEV) for b in range(B)]
+    vs = None if keqv else [W.kv_rows(wl, 0, b, "v", DEV) for b in range(B)]
+    # the current token (position L - 1) is each sequence's last generated row
+    k_new = torch.stack([k[:, -1] for k in ks]).contiguous()
+    v_new = None if keqv else torch.stack([v[:, -1] for v in vs]).contiguous()
+    older = [(s, e - 1) for s, e in spans]
+    stacks = []
+    for _ in range(2):
+        st = H.make_stack(wl, DEV)
+        H._append_span(st, 0, [k[:, :-1] for k in ks],
+                       None if keqv else [v[:, :-1] for v in vs], older, DEV)
+        stacks.append(st)
+    bufs = H.StepBuffers(wl, DEV)
+    fused = stacks[0].decode_append(0, bufs.q[0], k_new, v_new, bufs.lens, bufs.max_len)
+    pos = (bufs.lens - 1).to(torch.int32)
+    stacks[1].append_kv(0, k_new[:, None], None if keqv else v_new[:, None], pos,
+                        max_end_pos=bufs.max_len)
+    plain = stacks[1].decode(0, bufs.q[0], bufs.lens, bufs.max_len)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, plain)
+    assert torch.equal(stacks[0].cache, stacks[1].cache)
+    q = f64(bufs.q[0])
+    ref = np.stack([oracle_decode(wl, 0, b, q) for b in range(B)])
+    check_close(fused, ref, "fused decode")

@@ -255,6 +255,14 @@ def test_compute_calls_reject_before_launch(stack):
     assert _rc(G.g4attn_bind, h, None, 4096) == G.G4ATTN_ERR_NULL
     # shared layer cannot append
     assert _rc(G.g4attn_append_kv, h, 1, P, P, P, None, 2, 16, 16) == G.G4ATTN_ERR_SHARED_LAYER
+    # the fused decode step follows the append rules, then the decode ones
+    assert _rc(G.g4attn_decode_append, h, 1, P, P, P, P, 2, 10, P) == G.G4ATTN_ERR_SHARED_LAYER
+    assert _rc(G.g4attn_decode_append, h, 0, P, None, P, P, 2, 10, P) == G.G4ATTN_ERR_NULL
+    assert _rc(G.g4attn_decode_append, h, 0, P, P, None, P, 2, 10, P) == G.G4ATTN_ERR_NULL
+    assert _rc(G.g4attn_decode_append, h, 2, P, P, P, P, 2, 10, P) == G.G4ATTN_ERR_NULL
+    assert _rc(G.g4attn_decode_append, h, 0, P, P, P, P, 2, 10, P) == G.G4ATTN_ERR_UNBOUND
+    assert _rc(G.g4attn_decode_append, h, 2, P, P, None, P, 2, 10, P) == G.G4ATTN_ERR_UNBOUND
+    assert _rc(G.g4attn_decode_append, h, 3, P, P, P, P, 2, 10, P) == G.G4ATTN_ERR_RANGE
     # k_eq_v takes no V; others need one
     assert _rc(G.g4attn_append_kv, h, 2, P, P, P, None, 2, 16, 16) == G.G4ATTN_ERR_NULL
     assert _rc(G.g4attn_append_kv, h, 0, P, None, P, None, 2, 16, 16) == G.G4ATTN_ERR_NULL
