@@ -80,20 +80,17 @@ __device__ __forceinline__ void st16_coherent(float* p, f32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
 
-__device__ __forceinline__ f32x4 ld16_coherent_nowait(const float* p) {
-  f32x4 v;
-  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ void st_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float ld_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// 8 bytes read coherently at agent scope (an atomic load: the compiler tracks
+// its completion like any other load)
+__device__ __forceinline__ uint64_t ld8_coherent(const float* p) {
+  return __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Arrival of one split: returns true in the workgroup that arrived last.  All
@@ -141,95 +138,6 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
 // split merge: out[row] = sum_s w_s O_s / sum_s w_s l_s, w_s = 2^(m_s - max m)
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void ld8_coherent_nowait(const float* p, float& a, float& b) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  f32x2 v;
-  asm volatile("global_load_dwordx2 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
-  a = v[0];
-  b = v[1];
-}
-
-// In-kernel version, run by the last workgroup of a group to arrive.  All
-// (m, l) pairs are fetched in one batch, then the partial outputs in batches
-// of up to 8 splits per thread, so the merge costs a few memory round trips.
-// `ml` is LDS scratch for n_rows * n_splits * 2 floats.
-template <int D>
-__device__ void merge_rows_coherent(const float* part_o, const float* part_ml, size_t row0_part,
-                                    int n_rows, int n_splits, uint16_t* out,
-                                    const size_t* out_row_off, float* ml /*LDS*/,
-                                    float* inv_l /*LDS*/, int row_stride) {
-  // row r's split s lives at (row0_part + r * row_stride + s); n_splits <= row_stride in use
-  const int tid = threadIdx.x;
-  const int n_pairs = n_rows * n_splits;
-  {
-    constexpr int PER = 4;
-    float mv[PER], lv[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = tid + i * (int)blockDim.x;
-      const size_t src = row0_part + (size_t)(idx / n_splits) * row_stride + idx % n_splits;
-      if (idx < n_pairs) ld8_coherent_nowait(part_ml + src * 2, mv[i], lv[i]);
-    }
-    wait_vmem();
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = tid + i * (int)blockDim.x;
-      if (idx < n_pairs) {
-        ml[2 * idx] = mv[i];
-        ml[2 * idx + 1] = lv[i];
-      }
-    }
-    for (int idx = tid + PER * (int)blockDim.x; idx < n_pairs; idx += blockDim.x) {
-      const size_t src = row0_part + (size_t)(idx / n_splits) * row_stride + idx % n_splits;
-      ml[2 * idx] = ld_coherent(part_ml + src * 2);
-      ml[2 * idx + 1] = ld_coherent(part_ml + src * 2 + 1);
-    }
-  }
-  __syncthreads();
-  // weights in place of m: w_s = 2^(m_s - max m) over splits with l_s > 0
-  for (int r = tid; r < n_rows; r += blockDim.x) {
-    float* p = ml + 2 * r * n_splits;
-    float M = kNegInf;
-    for (int s = 0; s < n_splits; ++s)
-      if (p[2 * s + 1] > 0.f) M = fmaxf(M, p[2 * s]);
-    float lsum = 0.f;
-    for (int s = 0; s < n_splits; ++s) {
-      const float l = p[2 * s + 1];
-      const float w = l > 0.f ? fast_exp2(p[2 * s] - M) : 0.f;
-      p[2 * s] = w;
-      lsum += w * l;
-    }
-    inv_l[r] = lsum > 0.f ? 1.f / lsum : 0.f;
-  }
-  __syncthreads();
-  constexpr int D4 = D / 4;
-  constexpr int BATCH = 8;
-  for (int idx = tid; idx < n_rows * D4; idx += blockDim.x) {
-    const int r = idx / D4;
-    const int d = 4 * (idx - r * D4);
-    const float* po = part_o + (row0_part + (size_t)r * row_stride) * D + d;
-    const float* wr = ml + 2 * r * n_splits;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < n_splits; s0 += BATCH) {
-      f32x4 v[BATCH];
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i)
-        if (s0 + i < n_splits) v[i] = ld16_coherent_nowait(po + (size_t)(s0 + i) * D);
-      wait_vmem();
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i)
-        if (s0 + i < n_splits) {
-          const float w = wr[2 * (s0 + i)];
-          if (w != 0.f) acc += w * v[i];  // empty splits hold stale data: skip them
-        }
-    }
-    const float il = inv_l[r];
-    bf16x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = (__bf16)(acc[j] * il);
-    *reinterpret_cast<bf16x4*>(out + out_row_off[r] + d) = o;
-  }
-}
 
 // Stand-alone version for large decode merges (a kernel boundary separates
 // writer and reader, so ordinary loads see the partials).  A workgroup takes
@@ -366,7 +274,6 @@ struct Shape {
   // wave writes at once start on different LDS banks
   static constexpr int RED_STRIDE = D + 4;
   static constexpr int SLOT_BYTES = 16 * RED_STRIDE * 4;
-  static constexpr int MERGE_BYTES = (2 * 16 * kMaxDecodeSplits + 16) * 4;
   static constexpr int TR_BYTES = NW * TR_ELEMS * 2;
   static constexpr int Q_BYTES = KS * 512 * 2;
   // The waves combine their partial outputs in NSL reduction slots: one per
@@ -377,10 +284,10 @@ struct Shape {
   static constexpr int BUDGET = PREFILL ? 150 * 1024 : 78 * 1024;
   static constexpr int cmax(int a, int b) { return a > b ? a : b; }
   static constexpr bool fits(int n) {
-    return cmax(cmax(TR_BYTES, n * SLOT_BYTES), MERGE_BYTES) + Q_BYTES + 1024 <= BUDGET;
+    return cmax(TR_BYTES, n * SLOT_BYTES) + Q_BYTES + 1024 <= BUDGET;
   }
   static constexpr int NSL = fits(NW) ? NW : (NW % 2 == 0 && fits(NW / 2)) ? NW / 2 : 1;
-  static constexpr int LDS_BYTES = cmax(cmax(TR_BYTES, NSL * SLOT_BYTES), MERGE_BYTES);
+  static constexpr int LDS_BYTES = cmax(TR_BYTES, NSL * SLOT_BYTES);
 };
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -424,6 +331,22 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
   int new_pos = -1;  // fused append: position of the current token in this split
   // prefill only
   int row0 = 0, t_row = 0, h_row = 0;
+  // This wave's share of the query operand (sub-tiles w, w + NW, ...).  With
+  // head_dim 512 or in prefill it is loaded before anything that depends on
+  // the sequence lengths or positions, so it is in flight during the length
+  // read instead of queued behind the first key block (loads return in issue
+  // order); measured faster there and slightly slower for smaller decode
+  // heads, which load it after the first block.
+  constexpr bool EARLY_Q = PREFILL || D >= 512;
+  constexpr int QPW = (KS + NW - 1) / NW;
+  u32x4 qv[QPW];
+  auto load_q = [&]() {
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      const int s = w + i * NW;
+      if (s < KS) qv[i] = row_ok ? ldg16(qrow + 32 * s + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
   if constexpr (!PREFILL) {
     const DecodeArgs& a = da;
     split = blockIdx.x;
@@ -435,6 +358,9 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
     scale_log2 = a.scale_log2;
     head0 = g * a.G + hblk * 16;
     nrows = min(16, a.G - hblk * 16);
+    row_ok = c16 < nrows;
+    qrow = a.q + ((size_t)b * a.n_q + head0 + c16) * D;
+    if constexpr (EARLY_Q) load_q();
     int L = a.seq_lens[b];
     L = L < 0 ? 0 : (L > a.kv_max ? a.kv_max : L);
     const int lo = a.window > 0 ? max(0, L - a.window) : 0;
@@ -446,8 +372,6 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
     full_hi = r_end;
     row_lo = r_beg;
     row_hi = r_end;
-    row_ok = c16 < nrows;
-    qrow = a.q + ((size_t)b * a.n_q + head0 + c16) * D;
     if (a.k_new != nullptr && L > 0 && r_end == L) new_pos = L - 1;
   } else {
     const PrefillArgs& a = pa;
@@ -464,14 +388,16 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
     cap = a.cap;
     n_kv = a.n_kv;
     scale_log2 = a.scale_log2;
-    int start = a.start_pos[b];
-    start = start < 0 ? 0 : start;
     row0 = rowblk * 16;
     nrows = min(16, a.rows - row0);
     const int row = row0 + c16;
     row_ok = c16 < nrows;
     t_row = row_ok ? row / a.G : 0;
     h_row = row_ok ? row - t_row * a.G : 0;
+    qrow = a.q + (((size_t)b * a.T + t_row) * a.n_q + g * a.G + h_row) * D;
+    load_q();
+    int start = a.start_pos[b];
+    start = start < 0 ? 0 : start;
     const int p_first = start + row0 / a.G;
     const int p_last = start + (row0 + nrows - 1) / a.G;
     const int p_row = start + t_row;
@@ -484,7 +410,6 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
     full_hi = min(p_first + 1, r_end);
     row_lo = row_ok ? max(lo_of(p_row), r_beg) : 0;
     row_hi = row_ok ? min(p_row + 1, r_end) : 0;
-    qrow = a.q + (((size_t)b * a.T + t_row) * a.n_q + g * a.G + h_row) * D;
   }
   const int n_keys = r_end - r_beg;
   const uint16_t* kp = PREFILL ? pa.kp : da.kp;
@@ -549,12 +474,15 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
     load_k(blk_first + w);
     load_v(blk_first + w);
   }
+  if constexpr (!EARLY_Q) load_q();
 
   // queries as the B operand of S^T = K Q^T (column c16 = row, k-slots =
   // dims), kept in LDS in operand order: sub-tile s, lane L at (s*64 + L)*8
-  for (int s = w; s < KS; s += NW)
-    *reinterpret_cast<u32x4*>(&Qs[(s * 64 + lane) * 8]) =
-        row_ok ? ldg16(qrow + 32 * s + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    const int s = w + i * NW;
+    if (s < KS) *reinterpret_cast<u32x4*>(&Qs[(s * 64 + lane) * 8]) = qv[i];
+  }
   __syncthreads();
 
   f32x4 oacc[NDB];
@@ -831,42 +759,103 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
 
   if constexpr (!PREFILL) {
     const DecodeArgs& a = da;
-    // split partial: (m, l, O) in fp32
-    const size_t prow0 = ((size_t)b * a.n_q + head0) * a.n_splits + split;
-    for (int idx = tid; idx < nrows * D4; idx += NT) {
-      const int h = idx / D4;
-      const int d = 4 * (idx - h * D4);
-      const f32x4 v = red_sum(h, d);
-      float* dst = a.part_o + (prow0 + (size_t)h * a.n_splits) * D + d;
-      if (a.merge_in_kernel)
-        st16_coherent(dst, v);
-      else
-        *reinterpret_cast<f32x4*>(dst) = v;
-    }
-    if (tid < nrows) {
-      float* ml = a.part_ml + (prow0 + (size_t)tid * a.n_splits) * 2;
-      const float lval = n_keys > 0 ? hL[tid] : 0.f;
-      if (a.merge_in_kernel) {
-        st_coherent(ml, hM[tid]);
-        st_coherent(ml + 1, lval);
-      } else {
-        ml[0] = hM[tid];
-        ml[1] = lval;
+    // split partials: (m, l, O) in fp32; row h, split s at prow0 + h * n_splits + s
+    const size_t prow0 = ((size_t)b * a.n_q + head0) * a.n_splits;
+    auto publish = [&](bool coherent) {
+      for (int idx = tid; idx < nrows * D4; idx += NT) {
+        const int h = idx / D4;
+        const int d = 4 * (idx - h * D4);
+        const f32x4 v = red_sum(h, d);
+        float* dst = a.part_o + (prow0 + (size_t)h * a.n_splits + split) * D + d;
+        if (coherent)
+          st16_coherent(dst, v);
+        else
+          *reinterpret_cast<f32x4*>(dst) = v;
       }
+      if (tid < nrows) {
+        float* ml = a.part_ml + (prow0 + (size_t)tid * a.n_splits + split) * 2;
+        const float lval = n_keys > 0 ? hL[tid] : 0.f;
+        if (coherent) {
+          st_coherent(ml, hM[tid]);
+          st_coherent(ml + 1, lval);
+        } else {
+          ml[0] = hM[tid];
+          ml[1] = lval;
+        }
+      }
+    };
+    if (!a.merge_in_kernel) {  // merge_kernel follows
+      publish(false);
+      return;
     }
-    if (!a.merge_in_kernel) return;
+    // In-kernel merge: every split publishes its partial, waits for the
+    // stores to complete and takes an arrival ticket; the last to arrive
+    // merges (its own partial is still in LDS)
+    publish(true);
     wait_vmem();
-    int32_t* ctr = a.counters + ((size_t)b * a.n_kv + g) * a.n_hblk + hblk;
-    if (!arrive_last(ctr, n_used, &s_flag)) return;
-
-    float* wgt = reinterpret_cast<float*>(lds);  // 16 x n_splits (m, l) pairs
-    float* inv_l = wgt + 2 * 16 * kMaxDecodeSplits;
-    __shared__ size_t out_off[16];
-    if (tid < nrows) out_off[tid] = ((size_t)b * a.n_q + head0 + tid) * D;
-    __syncthreads();
-    merge_rows_coherent<D>(a.part_o, a.part_ml, ((size_t)b * a.n_q + head0) * a.n_splits,
-                           nrows, n_used, a.out, out_off, wgt, inv_l, a.n_splits);
-    if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const size_t grp = ((size_t)b * a.n_kv + g) * a.n_hblk + hblk;
+    if (!arrive_last(a.counters + grp, n_used, &s_flag)) return;
+    // out = sum_s w_s O_s / sum_s w_s l_s, w_s = 2^(m_s - max m), splits in
+    // index order (the result does not depend on which split arrived last);
+    // up to kBatch splits per memory round trip, rescaled between batches
+    constexpr int kBatch = 8;
+    for (int idx = tid; idx < nrows * D4; idx += NT) {
+      const int r = idx / D4;
+      const int d = 4 * (idx - r * D4);
+      const size_t prow = prow0 + (size_t)r * a.n_splits;
+      float M = kNegInf, lsum = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < n_used; s0 += kBatch) {
+        f32x4 v[kBatch];
+        float mv[kBatch], lv[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          // unconditional loads (all in flight at once); past the last split
+          // the batch's first one is read again and ignored, and the own
+          // split's slot is replaced below
+          const int s = s0 + i < n_used ? s0 + i : s0;
+          const uint64_t ml = ld8_coherent(a.part_ml + (prow + s) * 2);
+          const float* po = a.part_o + (prow + s) * D + d;
+          const uint64_t o0 = ld8_coherent(po), o1 = ld8_coherent(po + 2);
+          mv[i] = __builtin_bit_cast(float, (uint32_t)ml);
+          lv[i] = __builtin_bit_cast(float, (uint32_t)(ml >> 32));
+          v[i] = f32x4{__builtin_bit_cast(float, (uint32_t)o0),
+                       __builtin_bit_cast(float, (uint32_t)(o0 >> 32)),
+                       __builtin_bit_cast(float, (uint32_t)o1),
+                       __builtin_bit_cast(float, (uint32_t)(o1 >> 32))};
+        }
+        if (split >= s0 && split < s0 + kBatch) {
+          const int i = split - s0;
+          mv[i] = hM[r];
+          lv[i] = n_keys > 0 ? hL[r] : 0.f;
+          v[i] = red_sum(r, d);
+        }
+        float bm = M;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          if (s0 + i < n_used && lv[i] > 0.f) bm = fmaxf(bm, mv[i]);
+        if (bm != M) {
+          const float sc = fast_exp2(M - bm);  // 0 while nothing was added
+          acc *= sc;
+          lsum *= sc;
+          M = bm;
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          if (s0 + i < n_used && lv[i] > 0.f) {  // empty splits may hold stale data
+            const float wt = fast_exp2(mv[i] - M);
+            acc += wt * v[i];
+            lsum += wt * lv[i];
+          }
+      }
+      const float il = lsum > 0.f ? 1.f / lsum : 0.f;
+      bf16x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = (__bf16)(acc[j] * il);
+      *reinterpret_cast<bf16x4*>(a.out + ((size_t)b * a.n_q + head0 + r) * D + d) = o;
+    }
+    if (tid == 0)  // every split of the group has arrived: ready for the next call
+      __hip_atomic_store(a.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
