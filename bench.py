@@ -310,6 +310,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one 1 GiB device copy, the reference for HBM byte counters")
+    ap.add_argument("--main-only", action="store_true",
+                    help="skip the TP=2 rank stack and the fused-append step, which launch the "
+                         "decode kernels at other shapes (for per-kernel profiler averages)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention path here runs on a single "
@@ -336,8 +339,8 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     dec = bench_decode(args, stream)
-    rank = bench_rank_decode(args, stream)
-    fused = bench_fused_step(args, stream)
+    rank = None if args.main_only else bench_rank_decode(args, stream)
+    fused = None if args.main_only else bench_fused_step(args, stream)
     prefill = {}
     if not args.no_prefill:
         for p in (960, 4032):

@@ -331,20 +331,19 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
   int new_pos = -1;  // fused append: position of the current token in this split
   // prefill only
   int row0 = 0, t_row = 0, h_row = 0;
-  // This wave's share of the query operand (sub-tiles w, w + NW, ...).  With
-  // head_dim 512 or in prefill it is loaded before anything that depends on
-  // the sequence lengths or positions, so it is in flight during the length
-  // read instead of queued behind the first key block (loads return in issue
-  // order); measured faster there and slightly slower for smaller decode
-  // heads, which load it after the first block.
-  constexpr bool EARLY_Q = PREFILL || D >= 512;
+  int rot = 0;  // this row block's offset into its block range
+  // This wave's share of the query operand (sub-tiles w, w + NW, ...),
+  // loaded before anything that depends on the sequence lengths or
+  // positions: it is then in flight during the length read instead of queued
+  // behind the first key block (loads complete in issue order).
   constexpr int QPW = (KS + NW - 1) / NW;
   u32x4 qv[QPW];
   auto load_q = [&]() {
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
       const int s = w + i * NW;
-      if (s < KS) qv[i] = row_ok ? ldg16(qrow + 32 * s + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+      if (QPW * NW == KS || s < KS)
+        qv[i] = row_ok ? ldg16(qrow + 32 * s + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   if constexpr (!PREFILL) {
@@ -360,7 +359,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
     nrows = min(16, a.G - hblk * 16);
     row_ok = c16 < nrows;
     qrow = a.q + ((size_t)b * a.n_q + head0 + c16) * D;
-    if constexpr (EARLY_Q) load_q();
+    load_q();
     int L = a.seq_lens[b];
     L = L < 0 ? 0 : (L > a.kv_max ? a.kv_max : L);
     const int lo = a.window > 0 ? max(0, L - a.window) : 0;
@@ -406,6 +405,11 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
     r_end = min(p_last + 1, a.kv_max);
     blk_first = r_beg / KB;
     blk_end = r_end > r_beg ? (r_end + KB - 1) / KB : blk_first;
+    // The row blocks of one (sequence, KV head) read the same keys.  Each
+    // starts at a different place in the range, so that their first rounds
+    // together request every block once from HBM and later rounds hit in L2,
+    // instead of all of them waiting for the same first touch each round.
+    rot = (int)(((long long)rowblk * (blk_end - blk_first)) / a.n_rowblk);
     full_lo = lo_of(p_last);
     full_hi = min(p_first + 1, r_end);
     row_lo = row_ok ? max(lo_of(p_row), r_beg) : 0;
@@ -470,18 +474,29 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
       wait_vmem();
     }
   }
-  if (n_mine > 0) {
-    load_k(blk_first + w);
-    load_v(blk_first + w);
-  }
-  if constexpr (!EARLY_Q) load_q();
+  // block of the wave's j-th position in the range (j = w, w + NW, ...)
+  const int nblk = blk_end - blk_first;
+  auto phys = [&](int j) {
+    if constexpr (!PREFILL) {
+      return blk_first + j;
+    } else {
+      int x = j + rot;
+      x -= x >= nblk ? nblk : 0;
+      return blk_first + x;
+    }
+  };
+  // The first block's loads are issued on every path (a wave without blocks
+  // loads one of the range and ignores it): after a conditional load the
+  // compiler's wait for the queries would have to cover every load.
+  load_k(phys(n_mine > 0 ? w : 0));
+  load_v(phys(n_mine > 0 ? w : 0));
 
   // queries as the B operand of S^T = K Q^T (column c16 = row, k-slots =
   // dims), kept in LDS in operand order: sub-tile s, lane L at (s*64 + L)*8
 #pragma unroll
   for (int i = 0; i < QPW; ++i) {
     const int s = w + i * NW;
-    if (s < KS) *reinterpret_cast<u32x4*>(&Qs[(s * 64 + lane) * 8]) = qv[i];
+    if (QPW * NW == KS || s < KS) *reinterpret_cast<u32x4*>(&Qs[(s * 64 + lane) * 8]) = qv[i];
   }
   __syncthreads();
 
@@ -493,10 +508,9 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
   uint16_t* tr = reinterpret_cast<uint16_t*>(lds) + w * S::TR_ELEMS;  // k_eq_v only
 
   // one key block; `pf` (a bool, or std::true_type / std::false_type) says
-  // whether the wave's next block (blk + NW) is loaded
-  auto block = [&](const int blk, auto pf) {
+  // whether the wave's next block `nxt` is loaded
+  auto block = [&](const int blk, const int nxt, auto pf) {
     const bool PFX = pf;  // a compile-time constant where the caller passes a type
-    const int nxt = blk + NW;
     // the next block's address, computed before any compiler barrier below
     // (those make captured values be reloaded)
     const uint16_t* const kbn = kblock(nxt);
@@ -664,15 +678,15 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
   };
 
   if (n_mine > 0) {
-    int blk = blk_first + w;
+    int j = w;
     if constexpr (KEQV || D >= 512) {
       // k_eq_v: no older load is waited for after the next block's loads
       // are issued, so a run-time condition costs nothing.  head_dim 512 with
       // a V plane: a second copy of the body does not fit the registers.
-      for (int i = 1; i <= n_mine; ++i, blk += NW) block(blk, i < n_mine);
+      for (int i = 1; i <= n_mine; ++i, j += NW) block(phys(j), phys(i < n_mine ? j + NW : j), i < n_mine);
     } else {
-      for (int i = 1; i < n_mine; ++i, blk += NW) block(blk, std::true_type{});
-      block(blk, std::false_type{});
+      for (int i = 1; i < n_mine; ++i, j += NW) block(phys(j), phys(j + NW), std::true_type{});
+      block(phys(j), phys(j), std::false_type{});
     }
   }
 
