@@ -279,9 +279,10 @@ struct Shape {
   // The waves combine their partial outputs in NSL reduction slots: one per
   // wave (one barrier), one per pair of waves (two), or a single slot that
   // the waves add into one after another.  Slots share the LDS with the
-  // transpose area; a decode workgroup stays within what lets two of them
-  // share a CU, a prefill workgroup (one per CU) may use most of it.
-  static constexpr int BUDGET = PREFILL ? 150 * 1024 : 78 * 1024;
+  // transpose area.  Both grids are planned for one workgroup per CU, which
+  // may then use most of the LDS (the head_dim 512 decode combine takes one
+  // barrier instead of four; smaller shapes stay small enough for two).
+  static constexpr int BUDGET = 150 * 1024;
   static constexpr int cmax(int a, int b) { return a > b ? a : b; }
   static constexpr bool fits(int n) {
     return cmax(TR_BYTES, n * SLOT_BYTES) + Q_BYTES + 1024 <= BUDGET;

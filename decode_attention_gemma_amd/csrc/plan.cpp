@@ -84,15 +84,18 @@ int32_t check_layer(const g4attn_stack* st, int32_t layer) {
 
 // Decode split policy: splits hold a fixed number of key blocks, sized so
 // that a sequence of the longest (hinted) length uses enough splits for the
-// grid to cover every CU `wgs_per_cu` times; shorter sequences use fewer.
+// grid to give every CU one workgroup; shorter sequences use fewer.  (Two
+// workgroups per CU, which the registers allow, measured slower: the four
+// waves of one workgroup already keep enough loads in flight, and twice the
+// splits double the partial results and lengthen the merge.)
 // A split also writes rows x head_dim fp32 partial outputs (and reads them
 // back in the merge); splits are made long enough that these stay within
 // an eighth of the split's cache bytes (this binds where many query heads
 // share one KV head, e.g. 16 rows over 16-key k_eq_v blocks).
-void decode_splits(int keys_max, int KB, int pairs, int wgs_per_cu, int rows, int planes,
+void decode_splits(int keys_max, int KB, int pairs, int rows, int planes,
                    int* blocks_per_split, int* n_splits) {
   const int nb_max = (keys_max + KB - 1) / KB + 1;  // +1: alignment of the first block
-  const int target_wgs = 256 * wgs_per_cu;
+  const int target_wgs = 256;
   int ns = ceil_div(target_wgs, pairs);
   if (ns > g4::kMaxDecodeSplits) ns = g4::kMaxDecodeSplits;
   if (ns > nb_max) ns = nb_max;
@@ -363,9 +366,8 @@ int32_t decode_impl(const g4attn_stack* st, int32_t layer, const void* q, const 
   const int nh = G < 16 ? G : 16;
   const int keys_max = d.window > 0 && d.window < max_seq_len ? d.window : max_seq_len;
   g4::DecodeArgs a;
-  const int wgs_per_cu = g4::waves_per_simd(d.head_dim, d.k_eq_v != 0);
   const int KB = g4::decode_block(d.k_eq_v != 0);
-  decode_splits(keys_max, KB, batch * d.n_kv_heads * n_hblk, wgs_per_cu, nh, d.k_eq_v ? 1 : 2,
+  decode_splits(keys_max, KB, batch * d.n_kv_heads * n_hblk, nh, d.k_eq_v ? 1 : 2,
                 &a.blocks_per_split, &a.n_splits);
   a.merge_in_kernel =
       (int64_t)a.n_splits * nh * d.head_dim * 4 <= kInKernelMergeBytes ? 1 : 0;
