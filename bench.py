@@ -50,7 +50,7 @@ def kv_bytes(wl, layer):
     return keys * d.n_kv_heads * d.head_dim * 2 * (1 if d.k_eq_v else 2)
 
 
-DOMINANT_KERNEL = "attend_kernel<256, false, 4, false>"
+DOMINANT_KERNEL = "attend_kernel<256, false, 4, false, false>"
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "attend_12b_hbm_bytes.md")
 KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_gemma_amd", "csrc", "kernels.hip")
 
@@ -227,6 +227,31 @@ def bench_rank_decode(args, stream):
             "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def bench_paged_decode(args, stream):
+    """The 12B decode step through a paged cache: 64-slot pages in a seeded
+    random order over a pool of arbitrary bits, one block table for all
+    layers."""
+    import torch
+
+    from decode_attention_gemma_amd import harness as H, workloads as W
+
+    wl = W.g12b_decode()
+    log(f"[bench] setup {wl.name} (paged cache, 64-slot pages)")
+    st = H.make_paged_stack(wl, page_size=64, device="cuda")
+    H.fill_cache(st, wl, "cuda")
+    bufs = H.StepBuffers(wl, "cuda")
+    g = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream), stream)
+    ms = time_graph(g, args.warmup, args.steps)
+    step_bytes = sum(kv_bytes(wl, i) for i in range(wl.n_layers))
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    log(f"[bench] paged decode step {ms*1e3:.1f} us, {gbs:.0f} GB/s")
+    del st, bufs, g
+    torch.cuda.empty_cache()
+    return {"workload": wl.name + ", paged (64-slot pages, permuted)",
+            "us_per_step": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def bench_prefill(prefix, args, stream):
     import torch
 
@@ -311,8 +336,9 @@ def main():
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one 1 GiB device copy, the reference for HBM byte counters")
     ap.add_argument("--main-only", action="store_true",
-                    help="skip the TP=2 rank stack and the fused-append step, which launch the "
-                         "decode kernels at other shapes (for per-kernel profiler averages)")
+                    help="skip the TP=2 rank stack, the fused-append step and the paged step, "
+                         "which launch the decode kernels at other shapes or in other "
+                         "instances (for per-kernel profiler averages)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention path here runs on a single "
@@ -341,6 +367,7 @@ def main():
     dec = bench_decode(args, stream)
     rank = None if args.main_only else bench_rank_decode(args, stream)
     fused = None if args.main_only else bench_fused_step(args, stream)
+    paged = None if args.main_only else bench_paged_decode(args, stream)
     prefill = {}
     if not args.no_prefill:
         for p in (960, 4032):
@@ -383,6 +410,7 @@ def main():
         },
         "decode_step_with_append": fused,
         "tp2_rank_decode": rank,
+        "paged_decode": paged,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

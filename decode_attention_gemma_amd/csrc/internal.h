@@ -32,12 +32,13 @@ inline int decode_block(bool k_eq_v) { return k_eq_v ? 16 : 32; }
 
 // Waves per SIMD an attention kernel instance is built for: 2 (up to 256
 // registers per lane), or 1 where one wave needs more (head_dim 512 without
-// k_eq_v: its V block and accumulators alone take 256).  A decode workgroup
-// has one wave per SIMD, so this is also its workgroups per CU.  (Deeper
-// per-wave prefetch at one wave per SIMD measured slower on every layer
-// type: with a single wave per SIMD nothing hides its own latencies.)
-__host__ __device__ constexpr int waves_per_simd(int head_dim, bool k_eq_v) {
-  return head_dim >= 512 && !k_eq_v ? 1 : 2;
+// k_eq_v: its V block and accumulators alone take 256) or where the LDS
+// admits one workgroup per CU anyway (head_dim 512 decode, whose combine
+// takes a reduction slot per wave).  (Deeper per-wave prefetch at one wave
+// per SIMD measured slower on every layer type: with a single wave per SIMD
+// nothing hides its own latencies.)
+__host__ __device__ constexpr int waves_per_simd(int head_dim, bool k_eq_v, bool prefill) {
+  return head_dim >= 512 && (!k_eq_v || !prefill) ? 1 : 2;
 }
 
 // Byte offsets of element d of the K row / V row in one segment.
@@ -53,6 +54,25 @@ __host__ __device__ inline int64_t v_elem_offset(int64_t slot, int d, int D) {
   return ((blk * (D / 16) + d / 16) * 64 + q * 16 + d % 16) * 16 + j * 2;
 }
 
+// Paged cache: position p of sequence b lives in physical page
+// table[b * stride + p / page] at slot p % page.  A page holds `page` slots
+// (a multiple of 64) of every KV head of one owning layer: (page, head) is a
+// segment of page * D elements in the operand order of an unpaged segment.
+// table == nullptr: the unpaged layout (segment (b, head) of cap slots).
+struct PageTable {
+  const int32_t* table;  // [batch][stride] physical page ids, or nullptr
+  int stride;            // entries per sequence (= kv_max / page)
+  int page;              // slots per page
+  int n_pages;           // pages in each plane; ids are clamped into [0, n_pages)
+};
+
+// LDS entries for the page ids a workgroup's key range spans.
+constexpr int kMaxWgPages = 1024;
+
+__host__ __device__ inline int clamp_page(int id, int n_pages) {
+  return id < 0 ? 0 : (id >= n_pages ? n_pages - 1 : id);
+}
+
 struct AppendArgs {
   const uint16_t* k;  // [batch][n_new][n_kv][D]
   const uint16_t* v;  // same, or nullptr when the layer has no V plane
@@ -61,6 +81,7 @@ struct AppendArgs {
   const int32_t* start;
   const int32_t* nvalid;  // nullable
   int n_new, n_kv, D, cap, kv_max;
+  PageTable pt;
 };
 
 struct DecodeArgs {
@@ -84,6 +105,7 @@ struct DecodeArgs {
   int blocks_per_split, n_splits;
   int merge_in_kernel;  // 1: last arriving workgroup merges; 0: a merge kernel follows
   float scale_log2;     // scale * log2(e)
+  PageTable pt;
 };
 
 // Key blocks [first, end) of split `split` of a sequence whose visible keys
@@ -113,6 +135,7 @@ struct PrefillArgs {
   // n_rowblk blocks of kPrefillRows
   int rows, n_rowblk;
   float scale_log2;
+  PageTable pt;
 };
 
 struct MergeArgs {

@@ -118,10 +118,18 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   if (t >= nv) return;
   const int pos = a.start[b] + t;
   if (pos < 0 || pos >= a.kv_max) return;
-  const int slot = pos % a.cap;
   const int D = a.D;
   const size_t src = ((size_t)(b * a.n_new + t) * a.n_kv + g) * D;
-  const size_t seg = (size_t)(b * a.n_kv + g) * a.cap * D;  // elements
+  int slot;
+  size_t seg;  // elements
+  if (a.pt.table) {
+    const int pg = clamp_page(a.pt.table[(size_t)b * a.pt.stride + pos / a.pt.page], a.pt.n_pages);
+    slot = pos % a.pt.page;
+    seg = ((size_t)pg * a.n_kv + g) * a.pt.page * D;
+  } else {
+    slot = pos % a.cap;
+    seg = (size_t)(b * a.n_kv + g) * a.cap * D;
+  }
   // K: each 8-dim chunk is 16 contiguous bytes
   for (int c = threadIdx.x; c < D / 8; c += 64) {
     const int d = 8 * c;
@@ -293,8 +301,8 @@ struct Shape {
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D, bool KEQV, int NW, bool PREFILL>
-__global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kernel(
+template <int D, bool KEQV, int NW, bool PREFILL, bool PAGED>
+__global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void attend_kernel(
     DecodeArgs da, PrefillArgs pa) {
   // k_eq_v prefill stages each K sub-tile for the V^T transpose as soon as
   // its score MFMA has read it, and reloads the register with the next
@@ -419,9 +427,36 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
   const int n_keys = r_end - r_beg;
   const uint16_t* kp = PREFILL ? pa.kp : da.kp;
   const uint16_t* vp = PREFILL ? pa.vp : da.vp;
-  const size_t seg = (size_t)(b * n_kv + g) * cap * D;
-  const uint16_t* kseg = kp + seg;
-  const uint16_t* vseg = vp + seg;
+  const size_t seg = (size_t)(b * n_kv + g) * cap * D;  // unpaged segment
+
+  // Paged cache: the page ids of the workgroup's key range, read once into
+  // LDS (the range spans at most kMaxWgPages pages; the host checks).
+  __shared__ int pg_ids[PAGED ? kMaxWgPages : 1];
+  int pg_first = 0;
+  if constexpr (PAGED) {
+    const PageTable& pt = PREFILL ? pa.pt : da.pt;
+    pg_first = (blk_first * KB) / pt.page;
+    const int pg_last = blk_end > blk_first ? (blk_end * KB - 1) / pt.page : pg_first;
+    const int n_pg = min(pg_last - pg_first + 1, kMaxWgPages);
+    const int32_t* row = pt.table + (size_t)b * pt.stride;
+    for (int i = tid; i < n_pg; i += NW * 64)
+      pg_ids[i] = clamp_page(row[min(pg_first + i, pt.stride - 1)], pt.n_pages);
+    __syncthreads();
+  }
+  // element offset of the segment holding key block blk, and the block's
+  // first slot in it
+  auto seg_of = [&](int blk, int& slot0) -> size_t {
+    if constexpr (!PAGED) {
+      slot0 = (blk * KB) % cap;
+      return seg;
+    } else {
+      const int page = PREFILL ? pa.pt.page : da.pt.page;
+      const int pos0 = blk * KB;
+      slot0 = pos0 % page;
+      const int i = min(max(pos0 / page - pg_first, 0), kMaxWgPages - 1);
+      return ((size_t)pg_ids[i] * n_kv + g) * page * D;
+    }
+  };
 
   // ---- block loads.  The next block's K (and V) is loaded as soon as the
   // registers it lands in are free, so it overlaps the rest of the current
@@ -435,8 +470,9 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
   // this lane's address in the K sub-tile 0 of a block (sub-tile s of score
   // block sb follows at (sb * KS + s) * 512 elements)
   auto kblock = [&](int blk) {
-    const int slot0 = (blk * KB) % cap;
-    return kseg + (size_t)(slot0 / 16) * KS * 512 + lane * 8;
+    int slot0;
+    const size_t sg = seg_of(blk, slot0);
+    return kp + sg + (size_t)(slot0 / 16) * KS * 512 + lane * 8;
   };
   auto load_k = [&](int blk) {
     const uint16_t* kb = kblock(blk);
@@ -447,15 +483,16 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV)) void attend_kerne
   };
   auto load_v = [&](int blk) {
     if constexpr (!KEQV) {
-      const int slot0 = (blk * KB) % cap;
+      int slot0;
+      const uint16_t* vs = vp + seg_of(blk, slot0);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        vreg[db] = ldg16(vseg + ((size_t)(slot0 / 32) * NDB + db) * 512 + lane * 8);
+        vreg[db] = ldg16(vs + ((size_t)(slot0 / 32) * NDB + db) * 512 + lane * 8);
     }
   };
   const int n_mine = n_keys > 0 && blk_first + w < blk_end
                          ? (blk_end - (blk_first + w) + NW - 1) / NW : 0;  // blocks of this wave
-  if constexpr (!PREFILL) {
+  if constexpr (!PREFILL && !PAGED) {
     // Fused append: the wave that will read the current token's block writes
     // the token's K (and V) row into its cache slot and waits for the stores
     // before loading anything, so its loads see the row.  No other workgroup
@@ -878,7 +915,10 @@ template <int D, bool KEQV>
 hipError_t decode_launch(const DecodeArgs& a, int batch, hipStream_t s) {
   dim3 grid(a.n_splits, a.n_kv * a.n_hblk, batch);
   PrefillArgs none{};
-  hipLaunchKernelGGL((attend_kernel<D, KEQV, 4, false>), grid, dim3(256), 0, s, a, none);
+  if (a.pt.table)
+    hipLaunchKernelGGL((attend_kernel<D, KEQV, 4, false, true>), grid, dim3(256), 0, s, a, none);
+  else
+    hipLaunchKernelGGL((attend_kernel<D, KEQV, 4, false, false>), grid, dim3(256), 0, s, a, none);
   return hipGetLastError();
 }
 
@@ -890,7 +930,12 @@ hipError_t prefill_launch(const PrefillArgs& a, hipStream_t s) {
   const int n_log = a.n_rowblk * a.n_kv * a.batch;
   dim3 grid(8 * ((n_log + 7) / 8));
   DecodeArgs none{};
-  hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, true>), grid, dim3(NW * 64), 0, s, none, a);
+  if (a.pt.table)
+    hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, true, true>), grid, dim3(NW * 64), 0, s, none,
+                       a);
+  else
+    hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, true, false>), grid, dim3(NW * 64), 0, s, none,
+                       a);
   return hipGetLastError();
 }
 

@@ -31,6 +31,9 @@ struct LayerPlan {
 struct g4attn_stack {
   std::vector<LayerPlan> L;
   int max_batch = 0, kv_max = 0, max_chunk = 0;
+  // paged cache: pages of `page` slots, n_pages per plane, kv_max / page
+  // block-table entries per sequence
+  int paged = 0, page = 0, n_pages = 0;
   uint64_t cache_bytes = 0;
   uint64_t ws_ctr_off = 0, ws_ml_off = 0, ws_o_off = 0, ws_bytes = 0;
   uint64_t ctr_count = 0, ml_floats = 0, o_floats = 0;
@@ -119,8 +122,15 @@ extern "C" {
 
 const char* g4attn_last_error(void) { return g_err.c_str(); }
 
-int32_t g4attn_stack_create(const g4attn_layer_desc* layers, int32_t n_layers, int32_t max_batch,
-                            int32_t kv_max, int32_t max_chunk, g4attn_stack** out) {
+}  // extern "C"
+
+namespace {
+
+// page == 0: the unpaged layout.  Otherwise `page` slots per page and
+// n_pages pages per plane; kv_max is then the block table's positions.
+int32_t create_impl(const g4attn_layer_desc* layers, int32_t n_layers, int32_t max_batch,
+                    int32_t kv_max, int32_t max_chunk, int32_t page, int32_t n_pages,
+                    g4attn_stack** out) {
   if (!layers || !out) return fail(G4ATTN_ERR_NULL, "layers and out must be non-NULL");
   if (n_layers <= 0) return fail(G4ATTN_ERR_DESC, "n_layers must be positive");
   if (max_batch <= 0 || max_batch > 65535) return fail(G4ATTN_ERR_DESC, "max_batch %d", max_batch);
@@ -132,6 +142,9 @@ int32_t g4attn_stack_create(const g4attn_layer_desc* layers, int32_t n_layers, i
   st->max_batch = max_batch;
   st->kv_max = kv_max;
   st->max_chunk = max_chunk;
+  st->paged = page > 0;
+  st->page = page;
+  st->n_pages = n_pages;
   st->L.resize(n_layers);
 
   for (int i = 0; i < n_layers; ++i) {
@@ -187,9 +200,9 @@ int32_t g4attn_stack_create(const g4attn_layer_desc* layers, int32_t n_layers, i
   for (int i = 0; i < n_layers; ++i) {
     LayerPlan& p = st->L[i];
     if (p.owner != i) continue;
-    p.cap = layer_cap(p.d, kv_max, max_chunk);
-    const uint64_t plane =
-        (uint64_t)max_batch * p.d.n_kv_heads * (uint64_t)p.cap * p.d.head_dim * 2;
+    p.cap = st->paged ? page : layer_cap(p.d, kv_max, max_chunk);
+    const uint64_t plane = (uint64_t)(st->paged ? n_pages : max_batch) * p.d.n_kv_heads *
+                           (uint64_t)p.cap * p.d.head_dim * 2;
     p.k_off = off;
     off = align256(off + plane);
     if (p.d.k_eq_v) {
@@ -231,6 +244,35 @@ int32_t g4attn_stack_create(const g4attn_layer_desc* layers, int32_t n_layers, i
 
   *out = st;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t g4attn_stack_create(const g4attn_layer_desc* layers, int32_t n_layers, int32_t max_batch,
+                            int32_t kv_max, int32_t max_chunk, g4attn_stack** out) {
+  return create_impl(layers, n_layers, max_batch, kv_max, max_chunk, 0, 0, out);
+}
+
+int32_t g4attn_stack_create_paged(const g4attn_layer_desc* layers, int32_t n_layers,
+                                  int32_t max_batch, int32_t page_size, int32_t n_pages,
+                                  int32_t max_pages_per_seq, int32_t max_chunk,
+                                  g4attn_stack** out) {
+  if (page_size < 64 || page_size % 64 != 0 || page_size > (1 << 16))
+    return fail(G4ATTN_ERR_DESC, "page_size %d: a multiple of 64 in [64, 65536]", page_size);
+  if (n_pages <= 0) return fail(G4ATTN_ERR_DESC, "n_pages %d must be positive", n_pages);
+  if (max_pages_per_seq <= 0 || (int64_t)max_pages_per_seq * page_size > (1 << 24))
+    return fail(G4ATTN_ERR_DESC, "max_pages_per_seq %d x page_size %d must be in [1, 2^24]",
+                max_pages_per_seq, page_size);
+  const int64_t kv_max = (int64_t)max_pages_per_seq * page_size;
+  // pages one workgroup's key range may span (its LDS copy of the page ids)
+  if (max_chunk > 0 && (kv_max + max_chunk) / page_size + 2 > g4::kMaxWgPages)
+    return fail(G4ATTN_ERR_UNSUPPORTED,
+                "a key range of %lld positions spans more than %d pages of %d slots",
+                (long long)(kv_max + max_chunk), g4::kMaxWgPages - 2, page_size);
+  return create_impl(layers, n_layers, max_batch, (int32_t)kv_max, max_chunk, page_size, n_pages,
+                     out);
 }
 
 void g4attn_stack_destroy(g4attn_stack* stack) { delete stack; }
@@ -293,6 +335,9 @@ int32_t g4attn_kv_offset(const g4attn_stack* st, int32_t layer, int32_t b, int32
                          int64_t pos, int32_t d, int64_t* off_k, int64_t* off_v) {
   if (int32_t rc = check_layer(st, layer)) return rc;
   if (!off_k || !off_v) return fail(G4ATTN_ERR_NULL, "off_k and off_v must be non-NULL");
+  if (st->paged)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "paged stack: positions map through a block table "
+                                        "(g4attn_page_offset gives a page's layout)");
   const LayerPlan& p = st->L[layer];
   if (b < 0 || b >= st->max_batch || kv_head < 0 || kv_head >= p.d.n_kv_heads || pos < 0 ||
       pos >= st->kv_max || d < 0 || d >= p.d.head_dim)
@@ -306,10 +351,52 @@ int32_t g4attn_kv_offset(const g4attn_stack* st, int32_t layer, int32_t b, int32
   return ok();
 }
 
-int32_t g4attn_append_kv(const g4attn_stack* st, int32_t layer, const void* k, const void* v,
-                         const int32_t* start_pos, const int32_t* n_valid, int32_t batch,
-                         int32_t n_new, int32_t max_end_pos, void* stream) {
+int32_t g4attn_page_offset(const g4attn_stack* st, int32_t layer, int32_t page, int32_t kv_head,
+                           int32_t slot, int32_t d, int64_t* off_k, int64_t* off_v) {
   if (int32_t rc = check_layer(st, layer)) return rc;
+  if (!off_k || !off_v) return fail(G4ATTN_ERR_NULL, "off_k and off_v must be non-NULL");
+  if (!st->paged) return fail(G4ATTN_ERR_UNSUPPORTED, "stack is not paged");
+  const LayerPlan& p = st->L[layer];
+  if (page < 0 || page >= st->n_pages || kv_head < 0 || kv_head >= p.d.n_kv_heads || slot < 0 ||
+      slot >= st->page || d < 0 || d >= p.d.head_dim)
+    return fail(G4ATTN_ERR_RANGE, "(page %d, kv_head %d, slot %d, d %d) out of range", page,
+                kv_head, slot, d);
+  const int D = p.d.head_dim;
+  const int64_t seg = ((int64_t)page * p.d.n_kv_heads + kv_head) * st->page * D * 2;
+  *off_k = (int64_t)p.k_off + seg + g4::k_elem_offset(slot, d, D);
+  *off_v = p.d.k_eq_v ? *off_k : (int64_t)p.v_off + seg + g4::v_elem_offset(slot, d, D);
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+g4::PageTable page_table(const g4attn_stack* st, const int32_t* table) {
+  g4::PageTable t{};
+  if (st->paged) {
+    t.table = table;
+    t.stride = st->kv_max / st->page;
+    t.page = st->page;
+    t.n_pages = st->n_pages;
+  }
+  return t;
+}
+
+// The paged and unpaged entry points take the same arguments but for the
+// block table; each accepts only its own kind of stack.
+int32_t check_mode(const g4attn_stack* st, const int32_t* table, bool paged_call) {
+  if (paged_call && !st->paged)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "stack is not paged: use the unpaged entry point");
+  if (!paged_call && st->paged)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "stack is paged: use the _paged entry point");
+  if (paged_call && !table) return fail(G4ATTN_ERR_NULL, "block_table must be non-NULL");
+  return G4ATTN_OK;
+}
+
+int32_t append_impl(const g4attn_stack* st, int32_t layer, const void* k, const void* v,
+                    const int32_t* start_pos, const int32_t* n_valid, int32_t batch,
+                    int32_t n_new, int32_t max_end_pos, const int32_t* table, void* stream) {
   const LayerPlan& p = st->L[layer];
   if (p.owner != layer)
     return fail(G4ATTN_ERR_SHARED_LAYER, "layer %d reads layer %d's cache and writes none", layer,
@@ -337,9 +424,33 @@ int32_t g4attn_append_kv(const g4attn_stack* st, int32_t layer, const void* k, c
   a.D = p.d.head_dim;
   a.cap = p.cap;
   a.kv_max = st->kv_max;
+  a.pt = page_table(st, table);
   hipError_t e = g4::launch_append(a, batch, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(G4ATTN_ERR_HIP, "append launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t g4attn_append_kv(const g4attn_stack* st, int32_t layer, const void* k, const void* v,
+                         const int32_t* start_pos, const int32_t* n_valid, int32_t batch,
+                         int32_t n_new, int32_t max_end_pos, void* stream) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  if (int32_t rc = check_mode(st, nullptr, false)) return rc;
+  return append_impl(st, layer, k, v, start_pos, n_valid, batch, n_new, max_end_pos, nullptr,
+                     stream);
+}
+
+int32_t g4attn_append_kv_paged(const g4attn_stack* st, int32_t layer, const void* k,
+                               const void* v, const int32_t* start_pos, const int32_t* n_valid,
+                               int32_t batch, int32_t n_new, int32_t max_end_pos,
+                               const int32_t* block_table, void* stream) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  if (int32_t rc = check_mode(st, block_table, true)) return rc;
+  return append_impl(st, layer, k, v, start_pos, n_valid, batch, n_new, max_end_pos, block_table,
+                     stream);
 }
 
 }  // extern "C"
@@ -349,7 +460,7 @@ namespace {
 // Decode, optionally writing the current token's K / V rows first (k_new).
 int32_t decode_impl(const g4attn_stack* st, int32_t layer, const void* q, const void* k_new,
                     const void* v_new, const int32_t* seq_lens, int32_t batch,
-                    int32_t max_seq_len, void* out, void* stream) {
+                    int32_t max_seq_len, const int32_t* table, void* out, void* stream) {
   if (!q || !seq_lens || !out) return fail(G4ATTN_ERR_NULL, "q, seq_lens and out must be non-NULL");
   if (batch <= 0 || batch > st->max_batch)
     return fail(G4ATTN_ERR_RANGE, "batch %d not in [1, %d]", batch, st->max_batch);
@@ -389,6 +500,7 @@ int32_t decode_impl(const g4attn_stack* st, int32_t layer, const void* q, const 
   a.window = d.window;
   a.kv_max = st->kv_max;
   a.scale_log2 = d.scale * 1.4426950408889634f;
+  a.pt = page_table(st, table);
   hipError_t e = g4::launch_decode(d.head_dim, d.k_eq_v != 0, a, batch,
                                    static_cast<hipStream_t>(stream));
   if (e == hipSuccess && a.n_splits > 1 && !a.merge_in_kernel) {
@@ -419,7 +531,18 @@ int32_t g4attn_decode(const g4attn_stack* st, int32_t layer, const void* q,
                       const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, void* out,
                       void* stream) {
   if (int32_t rc = check_layer(st, layer)) return rc;
-  return decode_impl(st, layer, q, nullptr, nullptr, seq_lens, batch, max_seq_len, out, stream);
+  if (int32_t rc = check_mode(st, nullptr, false)) return rc;
+  return decode_impl(st, layer, q, nullptr, nullptr, seq_lens, batch, max_seq_len, nullptr, out,
+                     stream);
+}
+
+int32_t g4attn_decode_paged(const g4attn_stack* st, int32_t layer, const void* q,
+                            const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                            const int32_t* block_table, void* out, void* stream) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  if (int32_t rc = check_mode(st, block_table, true)) return rc;
+  return decode_impl(st, layer, q, nullptr, nullptr, seq_lens, batch, max_seq_len, block_table,
+                     out, stream);
 }
 
 int32_t g4attn_decode_append(const g4attn_stack* st, int32_t layer, const void* q,
@@ -433,13 +556,17 @@ int32_t g4attn_decode_append(const g4attn_stack* st, int32_t layer, const void* 
   if (!k_new) return fail(G4ATTN_ERR_NULL, "k_new must be non-NULL");
   if (p.d.k_eq_v && v_new) return fail(G4ATTN_ERR_NULL, "v_new must be NULL on a k_eq_v layer");
   if (!p.d.k_eq_v && !v_new) return fail(G4ATTN_ERR_NULL, "v_new must be non-NULL");
-  return decode_impl(st, layer, q, k_new, v_new, seq_lens, batch, max_seq_len, out, stream);
+  if (st->paged)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "the fused append is not built for paged stacks: "
+                                        "g4attn_append_kv_paged, then g4attn_decode_paged");
+  return decode_impl(st, layer, q, k_new, v_new, seq_lens, batch, max_seq_len, nullptr, out,
+                     stream);
 }
 
-int32_t g4attn_prefill(const g4attn_stack* st, int32_t layer, const void* q,
-                       const int32_t* start_pos, int32_t batch, int32_t n_tok,
-                       int32_t max_start_pos, void* out, void* stream) {
-  if (int32_t rc = check_layer(st, layer)) return rc;
+static int32_t prefill_impl(const g4attn_stack* st, int32_t layer, const void* q,
+                            const int32_t* start_pos, int32_t batch, int32_t n_tok,
+                            int32_t max_start_pos, const int32_t* table, void* out,
+                            void* stream) {
   if (!q || !start_pos || !out)
     return fail(G4ATTN_ERR_NULL, "q, start_pos and out must be non-NULL");
   if (batch <= 0 || batch > st->max_batch)
@@ -473,10 +600,29 @@ int32_t g4attn_prefill(const g4attn_stack* st, int32_t layer, const void* q,
   a.window = d.window;
   a.kv_max = st->kv_max;
   a.scale_log2 = d.scale * 1.4426950408889634f;
+  a.pt = page_table(st, table);
   hipError_t e = g4::launch_prefill(d.head_dim, d.k_eq_v != 0, a,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(G4ATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+int32_t g4attn_prefill(const g4attn_stack* st, int32_t layer, const void* q,
+                       const int32_t* start_pos, int32_t batch, int32_t n_tok,
+                       int32_t max_start_pos, void* out, void* stream) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  if (int32_t rc = check_mode(st, nullptr, false)) return rc;
+  return prefill_impl(st, layer, q, start_pos, batch, n_tok, max_start_pos, nullptr, out, stream);
+}
+
+int32_t g4attn_prefill_paged(const g4attn_stack* st, int32_t layer, const void* q,
+                             const int32_t* start_pos, int32_t batch, int32_t n_tok,
+                             int32_t max_start_pos, const int32_t* block_table, void* out,
+                             void* stream) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  if (int32_t rc = check_mode(st, block_table, true)) return rc;
+  return prefill_impl(st, layer, q, start_pos, batch, n_tok, max_start_pos, block_table, out,
+                      stream);
 }
 
 }  // extern "C"

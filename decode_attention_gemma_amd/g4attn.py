@@ -63,6 +63,17 @@ _SIGNATURES = {
                                        c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "g4attn_prefill": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32,
                                  c_int32, c_void_p, c_void_p]),
+    "g4attn_stack_create_paged": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                            c_int32, c_int32, POINTER(c_void_p)]),
+    "g4attn_page_offset": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                     POINTER(c_int64), POINTER(c_int64)]),
+    "g4attn_append_kv_paged": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                         c_void_p]),
+    "g4attn_decode_paged": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32,
+                                      c_void_p, c_void_p, c_void_p]),
+    "g4attn_prefill_paged": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32,
+                                       c_int32, c_void_p, c_void_p, c_void_p]),
     "g4attn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -224,6 +235,43 @@ def g4attn_prefill(stack: int, layer: int, q, start_pos, batch: int, n_tok: int,
                                  max_start_pos, _ptr(out), _stream(stream)))
 
 
+def g4attn_stack_create_paged(layers, max_batch: int, page_size: int, n_pages: int,
+                              max_pages_per_seq: int, max_chunk: int) -> int:
+    arr = layer_descs(layers)
+    out = c_void_p()
+    _check(load().g4attn_stack_create_paged(ctypes.cast(arr, c_void_p), len(layers), max_batch,
+                                            page_size, n_pages, max_pages_per_seq, max_chunk,
+                                            byref(out)))
+    return out.value
+
+
+def g4attn_page_offset(stack: int, layer: int, page: int, kv_head: int, slot: int,
+                       d: int) -> tuple[int, int]:
+    ok_, ov = c_int64(), c_int64()
+    _check(load().g4attn_page_offset(stack, layer, page, kv_head, slot, d, byref(ok_), byref(ov)))
+    return ok_.value, ov.value
+
+
+def g4attn_append_kv_paged(stack: int, layer: int, k, v, start_pos, n_valid, batch: int,
+                           n_new: int, max_end_pos: int, block_table, stream=None) -> None:
+    _check(load().g4attn_append_kv_paged(stack, layer, _ptr(k), _ptr(v), _ptr(start_pos),
+                                         _ptr(n_valid), batch, n_new, max_end_pos,
+                                         _ptr(block_table), _stream(stream)))
+
+
+def g4attn_decode_paged(stack: int, layer: int, q, seq_lens, batch: int, max_seq_len: int,
+                        block_table, out, stream=None) -> None:
+    _check(load().g4attn_decode_paged(stack, layer, _ptr(q), _ptr(seq_lens), batch, max_seq_len,
+                                      _ptr(block_table), _ptr(out), _stream(stream)))
+
+
+def g4attn_prefill_paged(stack: int, layer: int, q, start_pos, batch: int, n_tok: int,
+                         max_start_pos: int, block_table, out, stream=None) -> None:
+    _check(load().g4attn_prefill_paged(stack, layer, _ptr(q), _ptr(start_pos), batch, n_tok,
+                                       max_start_pos, _ptr(block_table), _ptr(out),
+                                       _stream(stream)))
+
+
 def g4attn_last_error() -> str:
     return load().g4attn_last_error().decode()
 
@@ -236,12 +284,25 @@ class Stack:
     """A planned layer stack with its cache and workspace on a torch device."""
 
     def __init__(self, layers, max_batch: int, kv_max: int, max_chunk: int = 64,
-                 device="cuda"):
+                 device="cuda", page_size=None, n_pages=None):
+        """page_size / n_pages: a paged cache (kv_max a multiple of page_size); its
+        calls then go through `block_table`, an int32 [max_batch, kv_max // page_size]
+        device tensor of page ids that the caller sets."""
         import torch
 
         self.layers = list(layers)
         self.max_batch, self.kv_max, self.max_chunk = max_batch, kv_max, max_chunk
-        self.handle = g4attn_stack_create(self.layers, max_batch, kv_max, max_chunk)
+        self.paged = page_size is not None
+        self.block_table = None
+        if self.paged:
+            if kv_max % page_size:
+                raise ValueError("kv_max must be a multiple of page_size")
+            self.page_size, self.n_pages = page_size, n_pages
+            self.max_pages = kv_max // page_size
+            self.handle = g4attn_stack_create_paged(self.layers, max_batch, page_size, n_pages,
+                                                    self.max_pages, max_chunk)
+        else:
+            self.handle = g4attn_stack_create(self.layers, max_batch, kv_max, max_chunk)
         self.cache_nbytes = g4attn_cache_bytes(self.handle)
         self.ws_nbytes = g4attn_workspace_bytes(self.handle)
         self.device = torch.device(device)
@@ -261,6 +322,14 @@ class Stack:
             self.close()
         except Exception:
             pass
+
+    def _table(self):
+        import torch
+
+        if self.block_table is None:
+            raise ValueError("a paged stack needs its block_table set")
+        _expect(self.block_table, (self.max_batch, self.max_pages), torch.int32, "block_table")
+        return self.block_table
 
     def owner(self, layer: int) -> int:
         return g4attn_resolve_owner(self.handle, layer)
@@ -282,7 +351,12 @@ class Stack:
             _expect(n_valid, (B,), torch.int32, "n_valid")
         if max_end_pos is None:
             raise ValueError("max_end_pos (host bound on start_pos + n_valid) is required")
-        g4attn_append_kv(self.handle, layer, k, v, start_pos, n_valid, B, T, max_end_pos, stream)
+        if self.paged:
+            g4attn_append_kv_paged(self.handle, layer, k, v, start_pos, n_valid, B, T,
+                                   max_end_pos, self._table(), stream)
+        else:
+            g4attn_append_kv(self.handle, layer, k, v, start_pos, n_valid, B, T, max_end_pos,
+                             stream)
 
     def decode(self, layer, q, seq_lens, max_seq_len, out=None, stream=None):
         """q: bf16 [B, n_q, D]; seq_lens: int32 [B] (keys incl. the current one)."""
@@ -295,7 +369,11 @@ class Stack:
         if out is None:
             out = torch.empty_like(q)
         _expect(out, tuple(q.shape), torch.bfloat16, "out")
-        g4attn_decode(self.handle, layer, q, seq_lens, B, max_seq_len, out, stream)
+        if self.paged:
+            g4attn_decode_paged(self.handle, layer, q, seq_lens, B, max_seq_len, self._table(),
+                                out, stream)
+        else:
+            g4attn_decode(self.handle, layer, q, seq_lens, B, max_seq_len, out, stream)
         return out
 
     def decode_append(self, layer, q, k_new, v_new, seq_lens, max_seq_len, out=None,
@@ -330,7 +408,11 @@ class Stack:
         if out is None:
             out = torch.empty_like(q)
         _expect(out, tuple(q.shape), torch.bfloat16, "out")
-        g4attn_prefill(self.handle, layer, q, start_pos, B, T, max_start_pos, out, stream)
+        if self.paged:
+            g4attn_prefill_paged(self.handle, layer, q, start_pos, B, T, max_start_pos,
+                                 self._table(), out, stream)
+        else:
+            g4attn_prefill(self.handle, layer, q, start_pos, B, T, max_start_pos, out, stream)
         return out
 
 

@@ -17,6 +17,24 @@ def make_stack(wl: W.Workload, device="cuda") -> Stack:
     return Stack(wl.layers, wl.batch, wl.kv_max, wl.max_chunk, device=device)
 
 
+def make_paged_stack(wl: W.Workload, page_size: int = 64, spare_pages: int = 8, device="cuda",
+                     seed: int = 1234) -> Stack:
+    """A paged stack for the workload: every position of every sequence gets a
+    page, the pages are a seeded random permutation of a pool with a few spare
+    pages, and the pool starts out holding arbitrary bits."""
+    kv_max = -(-wl.kv_max // page_size) * page_size
+    max_pages = kv_max // page_size
+    n_pages = wl.batch * max_pages + spare_pages
+    st = Stack(wl.layers, wl.batch, kv_max, wl.max_chunk, device=device, page_size=page_size,
+               n_pages=n_pages)
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(n_pages, generator=g)[: wl.batch * max_pages]
+    st.block_table = perm.to(torch.int32).reshape(wl.batch, max_pages).to(device)
+    gd = torch.Generator(device=device).manual_seed(seed)
+    st.cache.random_(0, 256, generator=gd)
+    return st
+
+
 def _append_span(stack: Stack, layer: int, rows_k, rows_v, spans, device):
     """Append per-sequence rows [n_kv, n_b, D] at positions spans[b] in chunks
     of at most max_chunk tokens (ragged sequences via n_valid)."""

@@ -15,6 +15,9 @@
  *          head_dim 512, K reused as V; sliding window 1024) and "The recipe"
  *          (a 64-token prefill bucket and a 1-token decode bucket sharing one
  *          resident cache).
+ *   [E4B]  "Gemma-4-E4B-it on AWS Inferentia2 -- Tensor-Parallel (TP=2)":
+ *          "Limitations" (single-stream batch-1 decode: neither continuous
+ *          batching nor a paged KV cache).
  *
  * Conventions for every call:
  *   - Return value: G4ATTN_OK (0) or a negative G4ATTN_ERR_* code.  On error
@@ -196,6 +199,51 @@ int32_t g4attn_decode_append(const g4attn_stack* stack, int32_t layer, const voi
 int32_t g4attn_prefill(const g4attn_stack* stack, int32_t layer, const void* q,
                        const int32_t* start_pos, int32_t batch, int32_t n_tok,
                        int32_t max_start_pos, void* out, void* stream);
+
+/*
+ * Paged KV cache, for continuous batching ([E4B] "Limitations" names its
+ * absence; [FR] closing section: batching as the next step).  Each owning
+ * layer's planes hold n_pages pages of page_size slots for every KV head.
+ * Position p of sequence b lives in page block_table[b * max_pages_per_seq +
+ * p / page_size] at slot p % page_size; all layers of a stack share one block
+ * table (page ids index each owning layer's own planes).  Within a page the
+ * slots of one KV head are laid out like a cap-slot segment of the unpaged
+ * layout.  There is no sliding-window ring: a sequence needs pages for the
+ * positions a call reads or writes, and pages wholly before every window it
+ * will read again may be reused by the caller.
+ *   page_size: a multiple of 64 in [64, 65536].
+ *   max_pages_per_seq: block-table entries per sequence; kv_max becomes
+ *       max_pages_per_seq * page_size.  A key range of kv_max + max_chunk
+ *       positions may span at most 1022 pages (else _UNSUPPORTED).
+ * Unpaged entry points reject a paged stack and the _paged ones an unpaged
+ * stack (G4ATTN_ERR_UNSUPPORTED); g4attn_decode_append and g4attn_kv_offset are
+ * unpaged only.  g4attn_layer_capacity returns page_size for a paged stack.
+ * Block tables are int32 device arrays [batch][max_pages_per_seq]; ids outside
+ * [0, n_pages) are clamped into it (wrong numbers, never an out-of-bounds
+ * access).  Errors: as for the unpaged calls, plus _NULL for a NULL table.
+ */
+int32_t g4attn_stack_create_paged(const g4attn_layer_desc* layers, int32_t n_layers,
+                                  int32_t max_batch, int32_t page_size, int32_t n_pages,
+                                  int32_t max_pages_per_seq, int32_t max_chunk,
+                                  g4attn_stack** out);
+/* Byte offsets in the cache of element d of (page, kv_head, slot)'s K row and
+ * V row for `layer`.  Errors: _NULL, _RANGE, _UNSUPPORTED (unpaged stack). */
+int32_t g4attn_page_offset(const g4attn_stack* stack, int32_t layer, int32_t page, int32_t kv_head,
+                           int32_t slot, int32_t d, int64_t* off_k, int64_t* off_v);
+/* g4attn_append_kv through a block table. */
+int32_t g4attn_append_kv_paged(const g4attn_stack* stack, int32_t layer, const void* k,
+                               const void* v, const int32_t* start_pos, const int32_t* n_valid,
+                               int32_t batch, int32_t n_new, int32_t max_end_pos,
+                               const int32_t* block_table, void* stream);
+/* g4attn_decode through a block table. */
+int32_t g4attn_decode_paged(const g4attn_stack* stack, int32_t layer, const void* q,
+                            const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                            const int32_t* block_table, void* out, void* stream);
+/* g4attn_prefill through a block table. */
+int32_t g4attn_prefill_paged(const g4attn_stack* stack, int32_t layer, const void* q,
+                             const int32_t* start_pos, int32_t batch, int32_t n_tok,
+                             int32_t max_start_pos, const int32_t* block_table, void* out,
+                             void* stream);
 
 /* Message of the last error on this thread ("" if none). */
 const char* g4attn_last_error(void);

@@ -293,3 +293,101 @@ def test_compute_calls_reject_before_launch(stack):
     assert _rc(G.g4attn_kv_offset, h, 0, 0, 0, 0, 64) == G.G4ATTN_ERR_RANGE
     assert _rc(G.g4attn_resolve_owner, h, 7) == G.G4ATTN_ERR_RANGE
     assert "out of range" in G.g4attn_last_error()
+
+
+# ---------------------------------------------------------------------------
+# paged cache plan (host only)
+# ---------------------------------------------------------------------------
+
+def _paged(layers, max_batch=2, page=64, n_pages=10, max_pages=4, max_chunk=16):
+    return G.g4attn_stack_create_paged(layers, max_batch, page, n_pages, max_pages, max_chunk)
+
+
+@pytest.mark.parametrize("page,n_pages,max_pages,code", [
+    (0, 4, 4, G.G4ATTN_ERR_DESC), (32, 4, 4, G.G4ATTN_ERR_DESC), (96, 4, 4, G.G4ATTN_ERR_DESC),
+    (64, 0, 4, G.G4ATTN_ERR_DESC), (64, 4, 0, G.G4ATTN_ERR_DESC),
+    (64, 4, 1100, G.G4ATTN_ERR_UNSUPPORTED),  # a key range would span > 1022 pages
+])
+def test_paged_create_rejects(page, n_pages, max_pages, code):
+    assert _rc(_paged, [_desc(4, 2, 64)], 2, page, n_pages, max_pages) == code
+
+
+def test_paged_offsets_match_an_unpaged_segment():
+    """Within a page the slots of one KV head sit exactly as in an unpaged
+    segment of the same capacity; pages are disjoint, equally spaced blocks of
+    each plane; shared layers read their owner's pages; k_eq_v has one plane."""
+    layers = [_desc(8, 2, 64, 40), _desc(8, 1, 128, 0, 1), _desc(4, 2, 64, 40, owner=0)]
+    page, n_pages = 64, 5
+    h = _paged(layers, max_batch=3, page=page, n_pages=n_pages, max_pages=4)
+    u = G.g4attn_stack_create([_desc(8, 2, 64, 0), _desc(8, 1, 128, 0, 1)], 1, page, 1)
+    try:
+        assert [G.g4attn_layer_capacity(h, i) for i in range(3)] == [page] * 3
+        total = G.g4attn_cache_bytes(h)
+        assert total >= n_pages * page * (2 * 64 * 2 * 2 + 1 * 128 * 2)
+        for layer, ulayer, D, nkv in ((0, 0, 64, 2), (1, 1, 128, 1)):
+            seen_k, seen_v = set(), set()
+            base_k = G.g4attn_page_offset(h, layer, 0, 0, 0, 0)[0]
+            ubase = G.g4attn_kv_offset(u, ulayer, 0, 0, 0, 0)
+            step = nkv * page * D * 2
+            for pg in range(n_pages):
+                for g in range(nkv):
+                    for s in range(0, page, 7):
+                        for d in range(0, D, 5):
+                            ok_, ov = G.g4attn_page_offset(h, layer, pg, g, s, d)
+                            uk, uv = G.g4attn_kv_offset(u, ulayer, 0, 0, s, d)
+                            # same in-segment layout as the unpaged segment
+                            assert ok_ - base_k == pg * step + g * page * D * 2 + (uk - ubase[0])
+                            if layers[layer].k_eq_v:
+                                assert ov == ok_
+                            else:
+                                assert ov - G.g4attn_page_offset(h, layer, 0, 0, 0, 0)[1] == \
+                                    pg * step + g * page * D * 2 + (uv - ubase[1])
+                            assert 0 <= ok_ < total and 0 <= ov < total
+                            assert ok_ not in seen_k
+                            seen_k.add(ok_)
+                            seen_v.add(ov)
+            if not layers[layer].k_eq_v:
+                assert not (seen_k & seen_v)
+        # the shared layer reads its owner's pages
+        for args in ((0, 0, 3, 9), (4, 1, 63, 63)):
+            assert G.g4attn_page_offset(h, 2, *args) == G.g4attn_page_offset(h, 0, *args)
+    finally:
+        G.g4attn_stack_destroy(h)
+        G.g4attn_stack_destroy(u)
+
+
+def test_paged_calls_reject_before_launch():
+    layers = [_desc(4, 2, 64, 8), _desc(4, 1, 64, 0, 1)]
+    h = _paged(layers, max_batch=2, page=64, n_pages=6, max_pages=2, max_chunk=16)
+    u = G.g4attn_stack_create(layers, 2, 128, 16)
+    P = 4096
+    try:
+        # each kind of stack takes only its own entry points
+        assert _rc(G.g4attn_decode, h, 0, P, P, 2, 10, P) == G.G4ATTN_ERR_UNSUPPORTED
+        assert _rc(G.g4attn_prefill, h, 0, P, P, 2, 16, 0, P) == G.G4ATTN_ERR_UNSUPPORTED
+        assert _rc(G.g4attn_append_kv, h, 0, P, P, P, None, 2, 16, 16) == G.G4ATTN_ERR_UNSUPPORTED
+        assert _rc(G.g4attn_decode_append, h, 0, P, P, P, P, 2, 10, P) == G.G4ATTN_ERR_UNSUPPORTED
+        assert _rc(G.g4attn_kv_offset, h, 0, 0, 0, 0, 0) == G.G4ATTN_ERR_UNSUPPORTED
+        assert _rc(G.g4attn_decode_paged, u, 0, P, P, 2, 10, P, P) == G.G4ATTN_ERR_UNSUPPORTED
+        assert _rc(G.g4attn_prefill_paged, u, 0, P, P, 2, 16, 0, P, P) == G.G4ATTN_ERR_UNSUPPORTED
+        assert _rc(G.g4attn_append_kv_paged, u, 0, P, P, P, None, 2, 16, 16, P) == \
+            G.G4ATTN_ERR_UNSUPPORTED
+        assert _rc(G.g4attn_page_offset, u, 0, 0, 0, 0, 0) == G.G4ATTN_ERR_UNSUPPORTED
+        # NULL block table, then the unpaged checks in their order
+        assert _rc(G.g4attn_decode_paged, h, 0, P, P, 2, 10, None, P) == G.G4ATTN_ERR_NULL
+        assert _rc(G.g4attn_prefill_paged, h, 0, P, P, 2, 16, 0, None, P) == G.G4ATTN_ERR_NULL
+        assert _rc(G.g4attn_append_kv_paged, h, 0, P, P, P, None, 2, 16, 16, None) == \
+            G.G4ATTN_ERR_NULL
+        assert _rc(G.g4attn_decode_paged, h, 0, P, P, 2, 10, P, P) == G.G4ATTN_ERR_UNBOUND
+        assert _rc(G.g4attn_decode_paged, h, 0, P, P, 2, 129, P, P) == G.G4ATTN_ERR_RANGE
+        assert _rc(G.g4attn_prefill_paged, h, 0, P, P, 2, 16, 113, P, P) == G.G4ATTN_ERR_RANGE
+        assert _rc(G.g4attn_append_kv_paged, h, 1, P, P, P, None, 2, 16, 16, P) == \
+            G.G4ATTN_ERR_NULL  # k_eq_v layer takes no V
+        # page hook ranges
+        assert _rc(G.g4attn_page_offset, h, 0, 6, 0, 0, 0) == G.G4ATTN_ERR_RANGE
+        assert _rc(G.g4attn_page_offset, h, 0, 0, 2, 0, 0) == G.G4ATTN_ERR_RANGE
+        assert _rc(G.g4attn_page_offset, h, 0, 0, 0, 64, 0) == G.G4ATTN_ERR_RANGE
+        assert _rc(G.g4attn_page_offset, h, 0, 0, 0, 0, 64) == G.G4ATTN_ERR_RANGE
+    finally:
+        G.g4attn_stack_destroy(h)
+        G.g4attn_stack_destroy(u)
