@@ -49,6 +49,7 @@ class LayerDesc:
     k_eq_v: int  # 1: V rows are the cached K rows
     kv_owner_layer: int  # -1 or own index = owns its cache
     scale: float
+    softcap: float = 0.0  # attention-logit cap c: s -> c tanh(s / c); 0 = none
 
 
 @dataclass

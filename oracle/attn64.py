@@ -11,6 +11,7 @@ query head and one query position at a time, in float64:
     out[h] = sum_k w_k * Vhat[k] / sum_k w_k,
     w_k    = exp(s_k - max_k s_k),
     s_k    = scale * <q[h], K[g(h), k]>,         k in the visible key set,
+    s_k   <- c * tanh(s_k / c)                     when the layer sets a logit cap c > 0,
 
 with the Gemma-4 specifics described on these pages:
 
@@ -35,7 +36,12 @@ function that uses it):
   * a KV-shared layer reads the cache of an earlier layer that owns its cache
     and has the same (n_kv_heads, head_dim, k_eq_v, window); the mask and the
     scale stay the reader's own;
-  * a query that sees no key returns zeros.
+  * a query that sees no key returns zeros;
+  * an attention-logit cap c > 0 (optional; the E4B Inferentia2 model card,
+    "Architecture", lists an attention softcap among the recipe's pieces but
+    gives no value) bends each scaled score s into c * tanh(s / c) before the
+    softmax, the same form the pages give for the final-logit cap; c = 0 or an
+    absent field means no cap.
 
 Every function here is pinned by CPU tests against closed forms, invariants,
 brute force and a library routine; none is "parity unpinned".
@@ -60,10 +66,10 @@ class OracleError(ValueError):
     """A layer stack that the method does not define."""
 
 
-def _field(desc, name):
+def _field(desc, name, default=None):
     if isinstance(desc, dict):
-        return desc[name]
-    return getattr(desc, name)
+        return desc[name] if default is None else desc.get(name, default)
+    return getattr(desc, name) if default is None else getattr(desc, name, default)
 
 
 def resolve_owners(layers) -> list[int]:
@@ -124,10 +130,14 @@ def kv_head_of(h: int, n_q: int, n_kv: int) -> int:
     return h // (n_q // n_kv)
 
 
-def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+           softcap: float = 0.0) -> np.ndarray:
     """Softmax attention of one query vector over the given key/value rows.
 
     q: [D]; K: [n, D]; V: [n, Dv]; all float64.  n == 0 gives zeros.
+    softcap c > 0: each scaled score s becomes c * tanh(s / c) before the
+    softmax (the cap form the pages give for Gemma-4's logits, here on the
+    attention scores); 0 leaves the scores as they are.
     """
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -135,6 +145,8 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndar
     if K.shape[0] == 0:
         return np.zeros(V.shape[1], dtype=np.float64)
     s = scale * (K @ q)
+    if softcap > 0:
+        s = softcap * np.tanh(s / softcap)
     w = np.exp(s - s.max())
     return (w @ V) / w.sum()
 
@@ -151,7 +163,7 @@ def decode_sequence(desc, q: np.ndarray, K: np.ndarray, V, n_keys: int,
     """One decode step of one sequence for one layer.
 
     desc: the reading layer's geometry (n_q_heads, n_kv_heads, head_dim,
-          window, k_eq_v, scale).
+          window, k_eq_v, scale, and optionally softcap).
     q:    [n_q, D] query of the current token.
     K, V: [n_kv, n, D] key/value rows of the owning layer's cache for the
           positions k_pos0 .. k_pos0 + n - 1 (V is ignored when k_eq_v).
@@ -167,6 +179,7 @@ def decode_sequence(desc, q: np.ndarray, K: np.ndarray, V, n_keys: int,
     window = int(_field(desc, "window"))
     keqv = int(_field(desc, "k_eq_v"))
     scale = float(_field(desc, "scale"))
+    softcap = float(_field(desc, "softcap", 0.0))
     D = int(_field(desc, "head_dim"))
     out = np.zeros((n_q, D), dtype=np.float64)
     if n_keys <= 0:
@@ -176,7 +189,7 @@ def decode_sequence(desc, q: np.ndarray, K: np.ndarray, V, n_keys: int,
         g = kv_head_of(h, n_q, n_kv)
         Kh = _rows(K[g], k_pos0, lo, hi)
         Vh = Kh if keqv else _rows(V[g], k_pos0, lo, hi)
-        out[h] = attend(q[h], Kh, Vh, scale)
+        out[h] = attend(q[h], Kh, Vh, scale, softcap)
     return out
 
 
@@ -198,6 +211,7 @@ def prefill_sequence(desc, q: np.ndarray, K: np.ndarray, V, start: int,
     window = int(_field(desc, "window"))
     keqv = int(_field(desc, "k_eq_v"))
     scale = float(_field(desc, "scale"))
+    softcap = float(_field(desc, "softcap", 0.0))
     D = int(_field(desc, "head_dim"))
     out = np.zeros((T, n_q, D), dtype=np.float64)
     n_keys = start + T
@@ -207,5 +221,5 @@ def prefill_sequence(desc, q: np.ndarray, K: np.ndarray, V, start: int,
             g = kv_head_of(h, n_q, n_kv)
             Kh = _rows(K[g], k_pos0, lo, hi)
             Vh = Kh if keqv else _rows(V[g], k_pos0, lo, hi)
-            out[t, h] = attend(q[t, h], Kh, Vh, scale)
+            out[t, h] = attend(q[t, h], Kh, Vh, scale, softcap)
     return out

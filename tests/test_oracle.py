@@ -322,6 +322,88 @@ def test_shared_reader_sees_owner_cache_with_its_own_query_and_scale():
 
 
 # --------------------------------------------------------------------------
+# attention-logit cap c: s -> c tanh(s / c) (optional descriptor field)
+# --------------------------------------------------------------------------
+
+def test_softcap_closed_form_where_tanh_is_one_half():
+    # tanh(ln(3) / 2) = (3 - 1) / (3 + 1) = 1/2 exactly.  With c = 2 and scale
+    # 0.5, q.k = 2 ln 3 gives s = ln 3 = c * ln(3)/2, capped to c/2 = 1; the
+    # other key has s = 0, capped to 0.  Weights e : 1.  Capping before the
+    # scale (tanh(ln 3) = 0.8), dropping the inner 1/c or the outer c all
+    # give other numbers.
+    q = np.array([1.0, 0.0])
+    K = np.array([[2.0 * math.log(3.0), 0.0], [0.0, 7.0]])
+    e = math.e
+    got = O.attend(q, K, np.eye(2), 0.5, softcap=2.0)
+    np.testing.assert_allclose(got, [e / (1 + e), 1 / (1 + e)], rtol=1e-14)
+
+
+def test_softcap_saturates_at_plus_minus_c():
+    # scores of +-1e6 are capped to exactly +-c: weights e^c : e^-c : e^-c
+    c = 1.5
+    q = np.array([1.0])
+    K = np.array([[1e6], [-1e6], [-2e6]])
+    got = O.attend(q, K, np.eye(3), 1.0, softcap=c)
+    z = math.exp(c) + 2 * math.exp(-c)
+    np.testing.assert_allclose(got, [math.exp(c) / z, math.exp(-c) / z, math.exp(-c) / z],
+                               rtol=1e-14)
+
+
+def test_softcap_weight_ratio_bounded_by_exp_2c():
+    # every capped score lies in (-c, c), so no weight exceeds another by more
+    # than e^(2c), however large the raw scores
+    D = n = 12
+    q, K = RNG.normal(size=D), RNG.normal(size=(n, D))
+    c = 0.75
+    w = O.attend(q, K, np.eye(n), 40.0, softcap=c)
+    assert w.max() / w.min() <= math.exp(2 * c) * (1 + 1e-12)
+    w_plain = O.attend(q, K, np.eye(n), 40.0)
+    assert w_plain.max() / w_plain.min() > math.exp(2 * c)  # the cap did bind
+
+
+def test_softcap_large_cap_reduces_to_plain_scores():
+    # c tanh(s/c) = s - s^3 / (3 c^2) + ...: with |s| <~ 5 and c = 1e4 the
+    # scores move by < 1e-6, so the output matches the uncapped one closely
+    D, n = 16, 40
+    q, K, V = RNG.normal(size=D), RNG.normal(size=(n, D)), RNG.normal(size=(n, D))
+    scale = 1 / math.sqrt(D)
+    plain = O.attend(q, K, V, scale)
+    np.testing.assert_allclose(O.attend(q, K, V, scale, softcap=1e4), plain, atol=1e-6, rtol=0)
+    assert np.abs(O.attend(q, K, V, scale, softcap=0.5) - plain).max() > 1e-2
+
+
+@pytest.mark.parametrize("window,keqv", [(5, 0), (0, 1)])
+def test_softcap_decode_and_prefill_match_explicit_loop(window, keqv):
+    # decode / prefill carry the reader's cap through grouping, mask and
+    # k_eq_v: compare with an explicit per-key loop over a boolean mask
+    D, nq, nkv, n = 8, 6, 2, 13
+    c, scale = 1.25, 0.8
+    d = W.LayerDesc(nq, nkv, D, window, keqv, -1, scale, c)
+    K, V = _seq(nkv, n, D)
+    q = RNG.normal(size=(3, nq, D))
+    start = n - 3
+
+    def loop(qv, g, p):
+        num, den = np.zeros(D), 0.0
+        for k in range(n):
+            if k > p or (window > 0 and p - k >= window):
+                continue
+            s = scale * float(np.dot(qv, K[g, k]))
+            w = math.exp(c * math.tanh(s / c))
+            num += w * (K[g, k] if keqv else V[g, k])
+            den += w
+        return num / den
+
+    dec = O.decode_sequence(d, q[2], K, V, n)
+    pre = O.prefill_sequence(d, q, K, V, start)
+    for h in range(nq):
+        g = h // (nq // nkv)
+        np.testing.assert_allclose(dec[h], loop(q[2, h], g, n - 1), atol=1e-12)
+        for t in range(3):
+            np.testing.assert_allclose(pre[t, h], loop(q[t, h], g, start + t), atol=1e-12)
+
+
+# --------------------------------------------------------------------------
 # workload geometry against the pages
 # --------------------------------------------------------------------------
 
