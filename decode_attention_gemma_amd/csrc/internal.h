@@ -105,6 +105,10 @@ struct DecodeArgs {
   int blocks_per_split, n_splits;
   int merge_in_kernel;  // 1: last arriving workgroup merges; 0: a merge kernel follows
   float scale_log2;     // scale * log2(e)
+  // attention-logit cap c (softcap != 0): score * log2(e) =
+  // cap_log2 * tanh(q.k * cap_in), cap_in = scale / c, cap_log2 = c * log2(e)
+  int softcap;
+  float cap_in, cap_log2;
   PageTable pt;
 };
 
@@ -135,6 +139,8 @@ struct PrefillArgs {
   // n_rowblk blocks of kPrefillRows
   int rows, n_rowblk;
   float scale_log2;
+  int softcap;  // as in DecodeArgs
+  float cap_in, cap_log2;
   PageTable pt;
 };
 

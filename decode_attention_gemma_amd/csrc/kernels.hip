@@ -53,6 +53,20 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// tanh for the attention-logit cap.  Below |x| = 1/16 its Taylor series
+// through x^7 (the next term is under 4e-13 relative there), so that a cap far
+// above the scores returns them unchanged; elsewhere tanh|x| = (1 - e)/(1 + e)
+// with e = exp(-2|x|), which tends to exactly +-1 as e underflows.  Relative
+// error about 1e-6 (exp2 and reciprocal hardware approximations).
+__device__ __forceinline__ float tanh_cap(float x) {
+  const float ax = __builtin_fabsf(x);
+  const float x2 = x * x;
+  const float p = x * (1.f + x2 * (-1.f / 3.f + x2 * (2.f / 15.f + x2 * (-17.f / 315.f))));
+  const float e = fast_exp2(-2.8853900817779268f * ax);  // exp(-2|x|)
+  const float t = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
+  return ax < 0.0625f ? p : __builtin_copysignf(t, x);
+}
+
 // Scheduling fence: the values in `acc` count as read and rewritten here, and
 // memory operations do not move across it.  Loads placed after it therefore
 // stay after the instructions that produced `acc`.
@@ -301,7 +315,7 @@ struct Shape {
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D, bool KEQV, int NW, bool PREFILL, bool PAGED>
+template <int D, bool KEQV, int NW, bool PREFILL, bool PAGED, bool CAP>
 __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void attend_kernel(
     DecodeArgs da, PrefillArgs pa) {
   // k_eq_v prefill stages each K sub-tile for the V^T transpose as soon as
@@ -335,6 +349,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
   bool row_ok;
   const uint16_t* qrow;     // this lane's query row
   float scale_log2;
+  float cap_in = 0.f, cap_log2 = 0.f;  // attention-logit cap (CAP)
   // decode only
   int split = 0, n_used = 1, head0 = 0, hblk = 0;
   int new_pos = -1;  // fused append: position of the current token in this split
@@ -364,6 +379,8 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
     cap = a.cap;
     n_kv = a.n_kv;
     scale_log2 = a.scale_log2;
+    cap_in = a.cap_in;
+    cap_log2 = a.cap_log2;
     head0 = g * a.G + hblk * 16;
     nrows = min(16, a.G - hblk * 16);
     row_ok = c16 < nrows;
@@ -396,6 +413,8 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
     cap = a.cap;
     n_kv = a.n_kv;
     scale_log2 = a.scale_log2;
+    cap_in = a.cap_in;
+    cap_log2 = a.cap_log2;
     row0 = rowblk * 16;
     nrows = min(16, a.rows - row0);
     const int row = row0 + c16;
@@ -607,7 +626,12 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
       for (int j = 0; j < 4; ++j) {
         const int kpos = pos0 + 16 * sb + 4 * q4 + j;
         const bool ok = row_ok & (kpos >= vis_lo) & (kpos < vis_hi);
-        sacc[sb][j] = ok ? sacc[sb][j] * scale_log2 : kNegInf;
+        float sv;
+        if constexpr (CAP)  // s * log2(e) with s = c tanh(scale q.k / c)
+          sv = cap_log2 * tanh_cap(sacc[sb][j] * cap_in);
+        else
+          sv = sacc[sb][j] * scale_log2;
+        sacc[sb][j] = ok ? sv : kNegInf;
         lmax = fmaxf(lmax, sacc[sb][j]);
       }
     }
@@ -911,14 +935,26 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
   }
 }
 
+// one attend_kernel launch, with or without the logit cap
+template <int D, bool KEQV, int NW, bool PREFILL, bool PAGED>
+void attend_launch(bool cap, dim3 grid, hipStream_t s, const DecodeArgs& da,
+                   const PrefillArgs& pa) {
+  if (cap)
+    hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, PREFILL, PAGED, true>), grid, dim3(NW * 64), 0,
+                       s, da, pa);
+  else
+    hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, PREFILL, PAGED, false>), grid, dim3(NW * 64),
+                       0, s, da, pa);
+}
+
 template <int D, bool KEQV>
 hipError_t decode_launch(const DecodeArgs& a, int batch, hipStream_t s) {
   dim3 grid(a.n_splits, a.n_kv * a.n_hblk, batch);
   PrefillArgs none{};
   if (a.pt.table)
-    hipLaunchKernelGGL((attend_kernel<D, KEQV, 4, false, true>), grid, dim3(256), 0, s, a, none);
+    attend_launch<D, KEQV, 4, false, true>(a.softcap != 0, grid, s, a, none);
   else
-    hipLaunchKernelGGL((attend_kernel<D, KEQV, 4, false, false>), grid, dim3(256), 0, s, a, none);
+    attend_launch<D, KEQV, 4, false, false>(a.softcap != 0, grid, s, a, none);
   return hipGetLastError();
 }
 
@@ -931,11 +967,9 @@ hipError_t prefill_launch(const PrefillArgs& a, hipStream_t s) {
   dim3 grid(8 * ((n_log + 7) / 8));
   DecodeArgs none{};
   if (a.pt.table)
-    hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, true, true>), grid, dim3(NW * 64), 0, s, none,
-                       a);
+    attend_launch<D, KEQV, NW, true, true>(a.softcap != 0, grid, s, none, a);
   else
-    hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, true, false>), grid, dim3(NW * 64), 0, s, none,
-                       a);
+    attend_launch<D, KEQV, NW, true, false>(a.softcap != 0, grid, s, none, a);
   return hipGetLastError();
 }
 

@@ -163,6 +163,11 @@ int32_t create_impl(const g4attn_layer_desc* layers, int32_t n_layers, int32_t m
       rc = fail(G4ATTN_ERR_DESC, "layer %d: k_eq_v must be 0 or 1", i);
     else if (!std::isfinite(d.scale))
       rc = fail(G4ATTN_ERR_DESC, "layer %d: scale is not finite", i);
+    else if (!(d.softcap == 0.f ||
+               (d.softcap > 0.f && std::isfinite(d.softcap) && std::isfinite(d.scale / d.softcap) &&
+                std::isfinite(d.softcap * 1.4426950408889634f))))
+      rc = fail(G4ATTN_ERR_DESC, "layer %d: softcap must be 0 or positive and finite, with "
+                "scale / softcap finite", i);
     else if (!head_dim_supported(d.head_dim))
       rc = fail(G4ATTN_ERR_UNSUPPORTED, "layer %d: head_dim %d not built (32/64/128/256/512)", i,
                 d.head_dim);
@@ -500,6 +505,9 @@ int32_t decode_impl(const g4attn_stack* st, int32_t layer, const void* q, const 
   a.window = d.window;
   a.kv_max = st->kv_max;
   a.scale_log2 = d.scale * 1.4426950408889634f;
+  a.softcap = d.softcap > 0.f ? 1 : 0;
+  a.cap_in = a.softcap ? d.scale / d.softcap : 0.f;
+  a.cap_log2 = a.softcap ? d.softcap * 1.4426950408889634f : 0.f;
   a.pt = page_table(st, table);
   hipError_t e = g4::launch_decode(d.head_dim, d.k_eq_v != 0, a, batch,
                                    static_cast<hipStream_t>(stream));
@@ -600,6 +608,9 @@ static int32_t prefill_impl(const g4attn_stack* st, int32_t layer, const void* q
   a.window = d.window;
   a.kv_max = st->kv_max;
   a.scale_log2 = d.scale * 1.4426950408889634f;
+  a.softcap = d.softcap > 0.f ? 1 : 0;
+  a.cap_in = a.softcap ? d.scale / d.softcap : 0.f;
+  a.cap_log2 = a.softcap ? d.softcap * 1.4426950408889634f : 0.f;
   a.pt = page_table(st, table);
   hipError_t e = g4::launch_prefill(d.head_dim, d.k_eq_v != 0, a,
                                     static_cast<hipStream_t>(stream));

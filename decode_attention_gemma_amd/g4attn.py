@@ -89,6 +89,7 @@ class LayerDescC(ctypes.Structure):
         ("k_eq_v", c_int32),
         ("kv_owner_layer", c_int32),
         ("scale", c_float),
+        ("softcap", c_float),
     ]
 
 
@@ -149,7 +150,7 @@ def layer_descs(layers) -> ctypes.Array:
     arr = (LayerDescC * len(layers))()
     for i, d in enumerate(layers):
         arr[i] = LayerDescC(d.n_q_heads, d.n_kv_heads, d.head_dim, d.window, d.k_eq_v,
-                            d.kv_owner_layer, d.scale)
+                            d.kv_owner_layer, d.scale, getattr(d, "softcap", 0.0))
     return arr
 
 

@@ -72,6 +72,13 @@ extern "C" {
  *       (n_kv_heads, head_dim, k_eq_v, window).  The layer then reads that
  *       cache and writes none ([FR] 2.1).
  *   scale: multiplies q.k before the softmax; must be finite.
+ *   softcap: attention-logit cap c.  0 = none; c > 0 replaces each scaled
+ *       score s by c * tanh(s / c) before the softmax (an attention softcap
+ *       is one of the recipe's pieces on the E4B Inferentia2 model card,
+ *       "Architecture", which gives no value; the c * tanh(x / c) form is the
+ *       one the pages give for Gemma-4's final-logit cap).  Must be 0, or
+ *       finite and positive with scale / c finite in fp32 (G4ATTN_ERR_DESC
+ *       otherwise).  A KV-shared layer uses its own cap, like its scale.
  */
 typedef struct g4attn_layer_desc {
   int32_t n_q_heads;
@@ -81,6 +88,7 @@ typedef struct g4attn_layer_desc {
   int32_t k_eq_v;
   int32_t kv_owner_layer;
   float scale;
+  float softcap;
 } g4attn_layer_desc;
 
 typedef struct g4attn_stack g4attn_stack; /* opaque, host-side plan */

@@ -42,8 +42,9 @@ def say(*a):
     sys.stdout.flush()
 
 
-def _desc(nq, nkv, d, window=0, keqv=0, owner=-1, scale=None):
-    return W.LayerDesc(nq, nkv, d, window, keqv, owner, scale if scale is not None else 1 / math.sqrt(d))
+def _desc(nq, nkv, d, window=0, keqv=0, owner=-1, scale=None, softcap=0.0):
+    return W.LayerDesc(nq, nkv, d, window, keqv, owner,
+                       scale if scale is not None else 1 / math.sqrt(d), softcap)
 
 
 def f64(t):
@@ -503,6 +504,61 @@ def test_peaked_softmax_many_running_max_updates(D, keqv, window):
     q = f64(bufs.q[0])
     ref = np.stack([oracle_prefill(wp, 0, b, q) for b in range(wp.batch)])
     check_close(bufs.out[0], ref, "peaked prefill")
+
+
+# ---------------------------------------------------------------------------
+# attention-logit cap: s -> c tanh(s / c)
+# ---------------------------------------------------------------------------
+
+SOFTCAP_GRID = [
+    # nq, nkv, D, window, keqv, cap, scale: the cap binds hard (scores of
+    # tens of units against c = 30 or 0.5), moderately, or not at all (1e4)
+    (16, 8, 256, 100, 0, 30.0, 3.0),
+    (16, 1, 512, 0, 1, 5.0, None),
+    (16, 1, 512, 0, 0, 30.0, 0.2),
+    (8, 2, 64, 0, 0, 0.5, 1.0),
+    (4, 2, 32, 8, 0, 1e4, None),
+    (12, 4, 64, 16, 1, 2.0, 0.5),
+]
+
+
+@pytest.mark.parametrize("nq,nkv,D,window,keqv,cap,scale", SOFTCAP_GRID)
+def test_softcap_decode_and_prefill(nq, nkv, D, window, keqv, cap, scale):
+    say(f"[gpu] softcap c={cap} scale={scale} nq={nq} nkv={nkv} D={D} W={window} k_eq_v={keqv}")
+    desc = _desc(nq, nkv, D, window, keqv, scale=scale, softcap=cap)
+    lens = [1, 17, 100, 333, 1029]
+    wl = _custom([desc], len(lens), "decode", kv_max=2048, seq_lens=lens, seed=11)
+    st, bufs = run_workload(wl)
+    q = f64(bufs.q[0])
+    ref = np.stack([oracle_decode(wl, 0, b, q) for b in range(wl.batch)])
+    check_close(bufs.out[0], ref, "softcap decode")
+    wp = _custom([desc], 3, "prefill", kv_max=2048, start_pos=[0, 37, 900], n_tok=64, seed=12)
+    st, bufs = run_workload(wp)
+    q = f64(bufs.q[0])
+    ref = np.stack([oracle_prefill(wp, 0, b, q) for b in range(wp.batch)])
+    check_close(bufs.out[0], ref, "softcap prefill")
+
+
+def test_softcap_is_the_readers_own_on_shared_and_paged_layers():
+    """A shared layer applies its own cap to the owner's cache (the owner has
+    none), through the unpaged and the paged cache."""
+    layers = [_desc(8, 2, 128, window=60), _desc(8, 2, 128, window=60, owner=0, scale=1.5,
+                                                   softcap=4.0)]
+    lens = [1, 59, 60, 61, 190]
+    wl = W.Workload(cfg_id=91, name="softcap shared", kind="decode", layers=layers,
+                    batch=len(lens), kv_max=256, max_chunk=64, seq_lens=lens, start_pos=None,
+                    n_tok=1)
+    for paged in (False, True):
+        st = H.make_paged_stack(wl, page_size=64, device=DEV, seed=3) if paged else \
+            H.make_stack(wl, DEV)
+        H.fill_cache(st, wl, DEV)
+        bufs = H.StepBuffers(wl, DEV)
+        H.run_step(st, bufs)
+        torch.cuda.synchronize()
+        for i in range(2):
+            q = f64(bufs.q[i])
+            ref = np.stack([oracle_decode(wl, i, b, q) for b in range(wl.batch)])
+            check_close(bufs.out[i], ref, f"softcap shared layer {i} paged={paged}")
 
 
 # ---------------------------------------------------------------------------

@@ -215,6 +215,10 @@ def _rc(fn, *args):
     ([W.LayerDesc(4, 2, 64, 0, 2, -1, 1.0)], G.G4ATTN_ERR_DESC),
     ([W.LayerDesc(4, 2, 64, 0, 0, -1, float("nan"))], G.G4ATTN_ERR_DESC),
     ([W.LayerDesc(4, 2, 64, 0, 0, -1, float("inf"))], G.G4ATTN_ERR_DESC),
+    ([W.LayerDesc(4, 2, 64, 0, 0, -1, 1.0, -1.0)], G.G4ATTN_ERR_DESC),          # softcap < 0
+    ([W.LayerDesc(4, 2, 64, 0, 0, -1, 1.0, float("nan"))], G.G4ATTN_ERR_DESC),
+    ([W.LayerDesc(4, 2, 64, 0, 0, -1, 1.0, float("inf"))], G.G4ATTN_ERR_DESC),
+    ([W.LayerDesc(4, 2, 64, 0, 0, -1, 1.0, 1e-45)], G.G4ATTN_ERR_DESC),         # scale/c overflows
     ([_desc(4, 2, 48)], G.G4ATTN_ERR_UNSUPPORTED),
     ([_desc(4, 2, 1024)], G.G4ATTN_ERR_UNSUPPORTED),
     ([_desc(4, 2, 64, owner=1), _desc(4, 2, 64)], G.G4ATTN_ERR_OWNER),       # later owner
@@ -228,6 +232,18 @@ def _rc(fn, *args):
 def test_create_rejects(layers, code):
     assert _rc(G.g4attn_stack_create, layers, 2, 64, 8) == code
     assert G.g4attn_last_error()
+
+
+def test_softcap_accepted_and_not_part_of_the_owner_match():
+    # a reader may cap its scores while its owner does not (the cap, like the
+    # scale, is the reader's own); 0 means no cap
+    layers = [W.LayerDesc(4, 2, 64, 8, 0, -1, 0.125, 0.0), W.LayerDesc(4, 2, 64, 8, 0, 0, 1.0, 4.0),
+              W.LayerDesc(4, 1, 64, 0, 1, -1, 0.125, 30.0)]
+    h = G.g4attn_stack_create(layers, 2, 64, 8)
+    try:
+        assert [G.g4attn_resolve_owner(h, i) for i in range(3)] == [0, 0, 2]
+    finally:
+        G.g4attn_stack_destroy(h)
 
 
 @pytest.mark.parametrize("mb,kv,mc", [(0, 64, 8), (2, 0, 8), (2, 64, 0), (-1, 64, 8)])
