@@ -12,6 +12,11 @@ Also reported on the same line:
   decode_step_with_append  the same step including the current token's
                 K/V write: append + decode per layer vs the fused call;
   tp2_rank_decode  one tensor-parallel rank (TP=2) of the same decode stack;
+  paged_decode  the same step through a paged cache (64-slot pages);
+  long_context_decode  the long-context ragged stack (B = 64, context
+                U{1..32768}, layers 20-47 KV-shared);
+  softcap_decode  the 12B decode step with an attention-logit cap on every
+                layer;
   prefill       the 12B-shaped 64-token prefill chunk stack (B = 4) after
                 960 and 4032 cached tokens, in TFLOP/s of visible-pair work;
   cpu_baseline  the fp64 oracle on a bounded sample of the same decode
@@ -227,6 +232,57 @@ def bench_rank_decode(args, stream):
             "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def bench_long_decode(args, stream):
+    """The long-context ragged decode stack: 12B geometry with layers 20-47
+    reading earlier owners' caches, B = 64, context U{1..32768}, 1% outliers."""
+    import torch
+
+    from decode_attention_gemma_amd import harness as H, workloads as W
+
+    wl = W.long_decode()
+    log(f"[bench] setup {wl.name}")
+    st = H.make_stack(wl, "cuda")
+    H.fill_cache(st, wl, "cuda")
+    bufs = H.StepBuffers(wl, "cuda")
+    g = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream), stream)
+    ms = time_graph(g, args.warmup, args.steps)
+    step_bytes = sum(kv_bytes(wl, i) for i in range(wl.n_layers))
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    log(f"[bench] long-context decode step {ms*1e3:.1f} us, {gbs:.0f} GB/s")
+    del st, bufs, g
+    torch.cuda.empty_cache()
+    return {"workload": wl.name + " (12B geometry, layers 20-47 KV-shared), B=64, "
+                                  "context U{1..32768}",
+            "us_per_step": round(ms * 1e3, 2), "kv_bytes_per_step": step_bytes,
+            "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def bench_softcap_decode(args, stream):
+    """The 12B decode stack with an attention-logit cap of 50 on every layer."""
+    import dataclasses
+
+    import torch
+
+    from decode_attention_gemma_amd import harness as H, workloads as W
+
+    wl = W.g12b_decode()
+    wl.layers = [dataclasses.replace(d, softcap=50.0) for d in wl.layers]
+    log(f"[bench] setup {wl.name} (logit cap 50)")
+    st = H.make_stack(wl, "cuda")
+    H.fill_cache(st, wl, "cuda")
+    bufs = H.StepBuffers(wl, "cuda")
+    g = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream), stream)
+    ms = time_graph(g, args.warmup, args.steps)
+    step_bytes = sum(kv_bytes(wl, i) for i in range(wl.n_layers))
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    log(f"[bench] softcap decode step {ms*1e3:.1f} us, {gbs:.0f} GB/s")
+    del st, bufs, g
+    torch.cuda.empty_cache()
+    return {"workload": wl.name + ", every layer capped at c = 50",
+            "us_per_step": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def bench_paged_decode(args, stream):
     """The 12B decode step through a paged cache: 64-slot pages in a seeded
     random order over a pool of arbitrary bits, one block table for all
@@ -368,6 +424,8 @@ def main():
     rank = None if args.main_only else bench_rank_decode(args, stream)
     fused = None if args.main_only else bench_fused_step(args, stream)
     paged = None if args.main_only else bench_paged_decode(args, stream)
+    long_ctx = None if args.main_only else bench_long_decode(args, stream)
+    capped = None if args.main_only else bench_softcap_decode(args, stream)
     prefill = {}
     if not args.no_prefill:
         for p in (960, 4032):
@@ -411,6 +469,8 @@ def main():
         "decode_step_with_append": fused,
         "tp2_rank_decode": rank,
         "paged_decode": paged,
+        "long_context_decode": long_ctx,
+        "softcap_decode": capped,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

@@ -283,7 +283,9 @@ __global__ __launch_bounds__(D / 4 > 64 ? D / 4 : 64) void merge_kernel(MergeArg
 
 template <int D, bool KEQV, int NW, bool SAG, bool PREFILL>
 struct Shape {
-  static constexpr int KB = KEQV ? 16 : 32;  // keys per block
+  // keys per block: 32, or 16 for k_eq_v prefill, whose staging area holds
+  // a whole block per wave
+  static constexpr int KB = SAG ? 16 : 32;
   static constexpr int NSB = KB / 16;        // 16-key score blocks per block
   static constexpr int KS = D / 32;          // 1 KiB K sub-tiles per 16 keys
   static constexpr int NDB = D / 16;         // 16-dim output blocks
@@ -291,7 +293,7 @@ struct Shape {
   // sub-tiles, or staged whole while the scores are computed (SAG)
   static constexpr int TRH = SAG || KS < 2 ? KS : KS / 2;
   static constexpr int NPH = KS / TRH;
-  static constexpr int TR_ELEMS = KEQV ? TRH * 512 : 0;  // per-wave transpose area
+  static constexpr int TR_ELEMS = KEQV ? NSB * TRH * 512 : 0;  // per-wave transpose area
   // cross-wave reduction rows are padded by 4 floats so that the 16 rows a
   // wave writes at once start on different LDS banks
   static constexpr int RED_STRIDE = D + 4;
@@ -699,41 +701,79 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
         load_v(nxt);
       }
     } else {
-      // The K block doubles as V: each phase stages TRH of its sub-tiles in
-      // this wave's LDS area in operand order, after which their registers
-      // take the next block's sub-tiles.  One transposing 64-bit read per
-      // lane then yields V[4q .. 4q+3][d0 + c] for a 16-dim block (the lane
-      // addresses key 4q + c/4, dims d0 + 4(c%4) .. +3).  LDS operations of
-      // one wave complete in order.  In a block that reaches outside
+      // The K block doubles as V: each phase stages TRH of the sub-tiles of
+      // every 16-key half in this wave's LDS area in operand order, after
+      // which their registers take the next block's sub-tiles.  One
+      // transposing 64-bit read per lane and half then yields
+      // V[4q .. 4q+3][d0 + c] of that half for a 16-dim block (the lane
+      // addresses key 4q + c/4, dims d0 + 4(c%4) .. +3).  With two halves
+      // the two reads form the A operand of a 16x16x32 MFMA whose k-slots
+      // carry keys 4q+j / 16+4q+j-4, the order of P^T above.  LDS operations
+      // of one wave complete in order.  In a block that reaches outside
       // [r_beg, r_end), the staged rows of those keys are overwritten with
-      // zeros (lane L of a sub-tile holds key L % 16).
-      const bool key_out = pos0 + c16 < r_beg || pos0 + c16 >= r_end;
+      // zeros (lane L of a sub-tile holds key L % 16 of its half).
+      bool key_out[NSB];
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        const int kpos = pos0 + 16 * sb + c16;
+        key_out[sb] = kpos < r_beg || kpos >= r_end;
+      }
+      bf16x8 pf8;
+      if constexpr (NSB == 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pf8[j] = pb[0][j];
+          pf8[4 + j] = pb[1][j];
+        }
+      }
 #pragma unroll
       for (int ph = 0; ph < S::NPH; ++ph) {
         if constexpr (!SAG) {
 #pragma unroll
-          for (int s = 0; s < S::TRH; ++s)
-            *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[0][ph * S::TRH + s];
+          for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+            for (int s = 0; s < S::TRH; ++s)
+              *reinterpret_cast<u32x4*>(tr + (sb * S::TRH + s) * 512 + lane * 8) =
+                  kreg[sb][ph * S::TRH + s];
         }
         if (!SAG && PFX) {
           asm volatile("" ::: "memory");  // after the staging writes
 #pragma unroll
-          for (int s = 0; s < S::TRH; ++s)
-            kreg[0][ph * S::TRH + s] = ldg16(kbn + (ph * S::TRH + s) * 512);
-        }
-        if (!vfull && key_out) {
+          for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-          for (int s = 0; s < S::TRH; ++s)
-            *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+            for (int s = 0; s < S::TRH; ++s)
+              kreg[sb][ph * S::TRH + s] = ldg16(kbn + (sb * KS + ph * S::TRH + s) * 512);
+        }
+        if (!vfull) {
+#pragma unroll
+          for (int sb = 0; sb < NSB; ++sb)
+            if (key_out[sb]) {
+#pragma unroll
+              for (int s = 0; s < S::TRH; ++s)
+                *reinterpret_cast<u32x4*>(tr + (sb * S::TRH + s) * 512 + lane * 8) =
+                    u32x4{0u, 0u, 0u, 0u};
+            }
         }
 #pragma unroll
         for (int dbl = 0; dbl < NDB / S::NPH; ++dbl) {
           const int dd = 16 * dbl + 4 * (c16 & 3);  // dim within the staged sub-tiles
           const int kk = 4 * q4 + (c16 >> 2);
           uint16_t* src = tr + (dd / 32) * 512 + ((dd % 32) / 8) * 128 + kk * 8 + (dd % 8);
-          const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src);
           const int db = ph * (NDB / S::NPH) + dbl;
-          oacc[db] = mfma16(__builtin_bit_cast(bf16x4, raw), pb[0], oacc[db]);
+          const s16x4 raw0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src);
+          if constexpr (NSB == 1) {
+            oacc[db] = mfma16(__builtin_bit_cast(bf16x4, raw0), pb[0], oacc[db]);
+          } else {
+            const s16x4 raw1 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + S::TRH * 512));
+            // composed as whole 32-bit words (element-wise bf16 inserts
+            // were miscompiled into duplicated registers)
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 w0 = __builtin_bit_cast(u32x2, raw0);
+            const u32x2 w1 = __builtin_bit_cast(u32x2, raw1);
+            const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
+            oacc[db] = mfma32(as_bf16x8(va), pf8, oacc[db]);
+          }
         }
       }
     }
