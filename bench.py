@@ -300,12 +300,31 @@ def bench_paged_decode(args, stream):
     ms = time_graph(g, args.warmup, args.steps)
     step_bytes = sum(kv_bytes(wl, i) for i in range(wl.n_layers))
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    log(f"[bench] paged decode step {ms*1e3:.1f} us, {gbs:.0f} GB/s")
+    # the same step with each token's K/V write fused into its decode launch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4321)
+    knew, vnew = [], []
+    for d in wl.layers:
+        shape = (wl.batch, d.n_kv_heads, d.head_dim)
+        knew.append(torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16))
+        vnew.append(None if d.k_eq_v else
+                    torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16))
+    sid = stream.cuda_stream
+
+    def fused():
+        for i in range(wl.n_layers):
+            st.decode_append(i, bufs.q[i], knew[i], vnew[i], bufs.lens, bufs.max_len, bufs.out[i],
+                             sid)
+
+    ms_fus = time_graph(graph_of(fused, stream), args.warmup, args.steps)
+    log(f"[bench] paged decode step {ms*1e3:.1f} us, {gbs:.0f} GB/s; "
+        f"with the fused token append {ms_fus*1e3:.1f} us")
     del st, bufs, g
     torch.cuda.empty_cache()
     return {"workload": wl.name + ", paged (64-slot pages, permuted)",
             "us_per_step": round(ms * 1e3, 2), "gbs": round(gbs, 1),
-            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "fused_decode_append_us": round(ms_fus * 1e3, 2)}
 
 
 def bench_prefill(prefix, args, stream):

@@ -513,21 +513,24 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
   };
   const int n_mine = n_keys > 0 && blk_first + w < blk_end
                          ? (blk_end - (blk_first + w) + NW - 1) / NW : 0;  // blocks of this wave
-  if constexpr (!PREFILL && !PAGED) {
+  if constexpr (!PREFILL) {
     // Fused append: the wave that will read the current token's block writes
     // the token's K (and V) row into its cache slot and waits for the stores
     // before loading anything, so its loads see the row.  No other workgroup
     // of this launch reads that slot as a visible key.  (Several head blocks
-    // of one KV head write the same bytes.)
+    // of one KV head write the same bytes.)  The slot's segment is the
+    // unpaged one or the page the block table maps the position to.
     if (new_pos >= 0 && w == (new_pos / KB - blk_first) % NW) {
-      const int slot = new_pos % cap;
+      int slot0;
+      const size_t sg = seg_of(new_pos / KB, slot0);
+      const int slot = slot0 + new_pos % KB;
       const size_t row = ((size_t)b * n_kv + g) * D;
-      uint16_t* kdst = da.kp + seg;
+      uint16_t* kdst = da.kp + sg;
       for (int c = lane; c < D / 8; c += 64)
         *reinterpret_cast<u32x4*>(kdst + k_elem_offset(slot, 8 * c, D) / 2) =
             ldg16(da.k_new + row + 8 * c);
       if constexpr (!KEQV) {
-        uint16_t* vdst = da.vp + seg;
+        uint16_t* vdst = da.vp + sg;
         for (int d = lane; d < D; d += 64) vdst[v_elem_offset(slot, d, D) / 2] = da.v_new[row + d];
       }
       wait_vmem();

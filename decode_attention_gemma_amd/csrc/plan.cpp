@@ -564,10 +564,25 @@ int32_t g4attn_decode_append(const g4attn_stack* st, int32_t layer, const void* 
   if (!k_new) return fail(G4ATTN_ERR_NULL, "k_new must be non-NULL");
   if (p.d.k_eq_v && v_new) return fail(G4ATTN_ERR_NULL, "v_new must be NULL on a k_eq_v layer");
   if (!p.d.k_eq_v && !v_new) return fail(G4ATTN_ERR_NULL, "v_new must be non-NULL");
-  if (st->paged)
-    return fail(G4ATTN_ERR_UNSUPPORTED, "the fused append is not built for paged stacks: "
-                                        "g4attn_append_kv_paged, then g4attn_decode_paged");
+  if (int32_t rc = check_mode(st, nullptr, false)) return rc;
   return decode_impl(st, layer, q, k_new, v_new, seq_lens, batch, max_seq_len, nullptr, out,
+                     stream);
+}
+
+int32_t g4attn_decode_append_paged(const g4attn_stack* st, int32_t layer, const void* q,
+                                   const void* k_new, const void* v_new,
+                                   const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                   const int32_t* block_table, void* out, void* stream) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  if (int32_t rc = check_mode(st, block_table, true)) return rc;
+  const LayerPlan& p = st->L[layer];
+  if (p.owner != layer)
+    return fail(G4ATTN_ERR_SHARED_LAYER, "layer %d reads layer %d's cache and writes none", layer,
+                p.owner);
+  if (!k_new) return fail(G4ATTN_ERR_NULL, "k_new must be non-NULL");
+  if (p.d.k_eq_v && v_new) return fail(G4ATTN_ERR_NULL, "v_new must be NULL on a k_eq_v layer");
+  if (!p.d.k_eq_v && !v_new) return fail(G4ATTN_ERR_NULL, "v_new must be non-NULL");
+  return decode_impl(st, layer, q, k_new, v_new, seq_lens, batch, max_seq_len, block_table, out,
                      stream);
 }
 

@@ -74,6 +74,9 @@ _SIGNATURES = {
                                       c_void_p, c_void_p, c_void_p]),
     "g4attn_prefill_paged": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32,
                                        c_int32, c_void_p, c_void_p, c_void_p]),
+    "g4attn_decode_append_paged": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                             c_void_p]),
     "g4attn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -266,6 +269,13 @@ def g4attn_decode_paged(stack: int, layer: int, q, seq_lens, batch: int, max_seq
                                       _ptr(block_table), _ptr(out), _stream(stream)))
 
 
+def g4attn_decode_append_paged(stack: int, layer: int, q, k_new, v_new, seq_lens, batch: int,
+                               max_seq_len: int, block_table, out, stream=None) -> None:
+    _check(load().g4attn_decode_append_paged(stack, layer, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                             _ptr(seq_lens), batch, max_seq_len,
+                                             _ptr(block_table), _ptr(out), _stream(stream)))
+
+
 def g4attn_prefill_paged(stack: int, layer: int, q, start_pos, batch: int, n_tok: int,
                          max_start_pos: int, block_table, out, stream=None) -> None:
     _check(load().g4attn_prefill_paged(stack, layer, _ptr(q), _ptr(start_pos), batch, n_tok,
@@ -394,8 +404,12 @@ class Stack:
         if out is None:
             out = torch.empty_like(q)
         _expect(out, tuple(q.shape), torch.bfloat16, "out")
-        g4attn_decode_append(self.handle, layer, q, k_new, v_new, seq_lens, B, max_seq_len, out,
-                             stream)
+        if self.paged:
+            g4attn_decode_append_paged(self.handle, layer, q, k_new, v_new, seq_lens, B,
+                                       max_seq_len, self._table(), out, stream)
+        else:
+            g4attn_decode_append(self.handle, layer, q, k_new, v_new, seq_lens, B, max_seq_len,
+                                 out, stream)
         return out
 
     def prefill(self, layer, q, start_pos, max_start_pos, out=None, stream=None):

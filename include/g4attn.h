@@ -224,8 +224,7 @@ int32_t g4attn_prefill(const g4attn_stack* stack, int32_t layer, const void* q,
  *       max_pages_per_seq * page_size.  A key range of kv_max + max_chunk
  *       positions may span at most 1022 pages (else _UNSUPPORTED).
  * Unpaged entry points reject a paged stack and the _paged ones an unpaged
- * stack (G4ATTN_ERR_UNSUPPORTED); g4attn_decode_append and g4attn_kv_offset are
- * unpaged only.  g4attn_layer_capacity returns page_size for a paged stack.
+ * stack (G4ATTN_ERR_UNSUPPORTED); g4attn_kv_offset is unpaged only.  g4attn_layer_capacity returns page_size for a paged stack.
  * Block tables are int32 device arrays [batch][max_pages_per_seq]; ids outside
  * [0, n_pages) are clamped into it (wrong numbers, never an out-of-bounds
  * access).  Errors: as for the unpaged calls, plus _NULL for a NULL table.
@@ -247,6 +246,16 @@ int32_t g4attn_append_kv_paged(const g4attn_stack* stack, int32_t layer, const v
 int32_t g4attn_decode_paged(const g4attn_stack* stack, int32_t layer, const void* q,
                             const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                             const int32_t* block_table, void* out, void* stream);
+/* g4attn_decode_append through a block table: the current token's K/V row is
+ * written at position seq_lens[b] - 1 of the page the table maps it to, then
+ * attended, in one launch.  The table must map that position.  The results
+ * (outputs and cache contents) are those of g4attn_append_kv_paged followed by
+ * g4attn_decode_paged; the errors those of g4attn_decode_append, plus _NULL
+ * for a NULL table. */
+int32_t g4attn_decode_append_paged(const g4attn_stack* stack, int32_t layer, const void* q,
+                                   const void* k_new, const void* v_new,
+                                   const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                   const int32_t* block_table, void* out, void* stream);
 /* g4attn_prefill through a block table. */
 int32_t g4attn_prefill_paged(const g4attn_stack* stack, int32_t layer, const void* q,
                              const int32_t* start_pos, int32_t batch, int32_t n_tok,

@@ -611,6 +611,50 @@ def test_fused_decode_step_equals_append_then_decode(nq, nkv, D, window, keqv, l
     check_close(fused, ref, "fused decode")
 
 
+@pytest.mark.parametrize("nq,nkv,D,window,keqv,lens,kv_max,max_chunk,page", [
+    (16, 8, 256, 100, 0, [1, 33, 64, 129, 400], 512, 64, 64),
+    (16, 1, 512, 0, 1, [1, 16, 17, 700, 2049], 4096, 64, 128),
+    (12, 4, 64, 16, 1, [1, 16, 40, 95], 256, 16, 64),
+    (32, 1, 64, 0, 0, [3, 200, 513], 1024, 64, 192),
+])
+def test_paged_fused_decode_step_equals_append_then_decode(nq, nkv, D, window, keqv, lens,
+                                                           kv_max, max_chunk, page):
+    """g4attn_decode_append_paged == g4attn_append_kv_paged + g4attn_decode_paged
+    through the same permuted block table over a pool of arbitrary bits:
+    outputs and the whole pool bit-identical; outputs match the oracle."""
+    say(f"[gpu] paged fused decode nq={nq} nkv={nkv} D={D} W={window} k_eq_v={keqv} "
+        f"lens={lens} page={page}")
+    desc = _desc(nq, nkv, D, window, keqv)
+    wl = _custom([desc], len(lens), "decode", kv_max=kv_max, max_chunk=max_chunk, seq_lens=lens)
+    B = wl.batch
+    spans = [W.kv_span(wl, 0, b) for b in range(B)]
+    ks = [W.kv_rows(wl, 0, b, "k", DEV) for b in range(B)]
+    vs = None if keqv else [W.kv_rows(wl, 0, b, "v", DEV) for b in range(B)]
+    k_new = torch.stack([k[:, -1] for k in ks]).contiguous()
+    v_new = None if keqv else torch.stack([v[:, -1] for v in vs]).contiguous()
+    older = [(s, e - 1) for s, e in spans]
+    stacks = []
+    for _ in range(2):  # same seed: same block table and the same pool bits
+        st = H.make_paged_stack(wl, page_size=page, device=DEV, seed=21)
+        H._append_span(st, 0, [k[:, :-1] for k in ks],
+                       None if keqv else [v[:, :-1] for v in vs], older, DEV)
+        stacks.append(st)
+    torch.cuda.synchronize()
+    assert torch.equal(stacks[0].cache, stacks[1].cache)
+    bufs = H.StepBuffers(wl, DEV)
+    fused = stacks[0].decode_append(0, bufs.q[0], k_new, v_new, bufs.lens, bufs.max_len)
+    pos = (bufs.lens - 1).to(torch.int32)
+    stacks[1].append_kv(0, k_new[:, None], None if keqv else v_new[:, None], pos,
+                        max_end_pos=bufs.max_len)
+    plain = stacks[1].decode(0, bufs.q[0], bufs.lens, bufs.max_len)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, plain)
+    assert torch.equal(stacks[0].cache, stacks[1].cache)
+    q = f64(bufs.q[0])
+    ref = np.stack([oracle_decode(wl, 0, b, q) for b in range(B)])
+    check_close(fused, ref, "paged fused decode")
+
+
 # ---------------------------------------------------------------------------
 # paged cache: the same kernels through a block table
 # ---------------------------------------------------------------------------

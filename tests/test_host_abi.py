@@ -389,6 +389,16 @@ def test_paged_calls_reject_before_launch():
         assert _rc(G.g4attn_append_kv_paged, u, 0, P, P, P, None, 2, 16, 16, P) == \
             G.G4ATTN_ERR_UNSUPPORTED
         assert _rc(G.g4attn_page_offset, u, 0, 0, 0, 0, 0) == G.G4ATTN_ERR_UNSUPPORTED
+        assert _rc(G.g4attn_decode_append_paged, u, 0, P, P, P, P, 2, 10, P, P) == \
+            G.G4ATTN_ERR_UNSUPPORTED
+        assert _rc(G.g4attn_decode_append_paged, h, 0, P, P, P, P, 2, 10, None, P) == \
+            G.G4ATTN_ERR_NULL
+        assert _rc(G.g4attn_decode_append_paged, h, 1, P, P, P, P, 2, 10, P, P) == \
+            G.G4ATTN_ERR_NULL  # k_eq_v layer takes no v_new
+        assert _rc(G.g4attn_decode_append_paged, h, 0, P, P, P, None, 2, 10, P, P) == \
+            G.G4ATTN_ERR_NULL  # a V plane needs v_new
+        assert _rc(G.g4attn_decode_append_paged, h, 0, P, P, P, P, 2, 10, P, P) == \
+            G.G4ATTN_ERR_UNBOUND
         # NULL block table, then the unpaged checks in their order
         assert _rc(G.g4attn_decode_paged, h, 0, P, P, 2, 10, None, P) == G.G4ATTN_ERR_NULL
         assert _rc(G.g4attn_prefill_paged, h, 0, P, P, 2, 16, 0, None, P) == G.G4ATTN_ERR_NULL
