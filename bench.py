@@ -17,8 +17,10 @@ Also reported on the same line:
                 U{1..32768}, layers 20-47 KV-shared);
   softcap_decode  the 12B decode step with an attention-logit cap on every
                 layer;
+  small_decode  the launch-bound tiny 2-layer and E4B-shaped 12-layer stacks;
   prefill       the 12B-shaped 64-token prefill chunk stack (B = 4) after
-                960 and 4032 cached tokens, in TFLOP/s of visible-pair work;
+                0, 960 and 4032 cached tokens, in TFLOP/s of visible-pair work
+                (prefix 0 is launch-bound: read its us per step);
   cpu_baseline  the fp64 oracle on a bounded sample of the same decode
                 workload, on the host cores.
 
@@ -257,6 +259,33 @@ def bench_long_decode(args, stream):
             "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def bench_small_decode(args, stream):
+    """The launch-bound decode stacks: the tiny 2-layer stack and the E4B-shaped
+    12-layer stack with KV sharing (B = 1, context 511), in us per step."""
+    import torch
+
+    from decode_attention_gemma_amd import harness as H, workloads as W
+
+    out = {}
+    for key, mk in (("tiny_2layer", W.tiny_stack), ("e4b_12layer", W.e4b_decode)):
+        wl = mk()
+        log(f"[bench] setup {wl.name}")
+        st = H.make_stack(wl, "cuda")
+        H.fill_cache(st, wl, "cuda")
+        bufs = H.StepBuffers(wl, "cuda")
+        g = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream), stream)
+        ms = time_graph(g, args.warmup, max(args.steps, 50))
+        step_bytes = sum(kv_bytes(wl, i) for i in range(wl.n_layers))
+        log(f"[bench] {wl.name}: {ms*1e3:.1f} us/step, {step_bytes/ms/1e6:.0f} GB/s")
+        out[key] = {"workload": wl.name, "us_per_step": round(ms * 1e3, 2),
+                    "us_per_layer": round(ms * 1e3 / wl.n_layers, 2),
+                    "kv_bytes_per_step": step_bytes,
+                    "gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1)}
+        del st, bufs, g
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_softcap_decode(args, stream):
     """The 12B decode stack with an attention-logit cap of 50 on every layer."""
     import dataclasses
@@ -445,9 +474,10 @@ def main():
     paged = None if args.main_only else bench_paged_decode(args, stream)
     long_ctx = None if args.main_only else bench_long_decode(args, stream)
     capped = None if args.main_only else bench_softcap_decode(args, stream)
+    small = None if args.main_only else bench_small_decode(args, stream)
     prefill = {}
     if not args.no_prefill:
-        for p in (960, 4032):
+        for p in ((960, 4032) if args.main_only else (0, 960, 4032)):
             prefill[f"prefix_{p}"] = bench_prefill(p, args, stream)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec)
 
@@ -490,6 +520,7 @@ def main():
         "paged_decode": paged,
         "long_context_decode": long_ctx,
         "softcap_decode": capped,
+        "small_decode": small,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

@@ -104,6 +104,9 @@ void decode_splits(int keys_max, int KB, int pairs, int rows, int planes,
   if (ns > nb_max) ns = nb_max;
   if (ns < 1) ns = 1;
   int bps = ceil_div(nb_max, ns);
+  // at least one block for each of a workgroup's 4 waves (short contexts,
+  // few sequences: fewer, fuller splits and a smaller merge)
+  if (bps < 4) bps = nb_max < 4 ? nb_max : 4;
   // partial bytes per split: rows * D * 4; cache bytes per block: KB * D * 2 * planes
   const int min_bps = ceil_div(8 * rows * 4, KB * 2 * planes);
   if (ns > 1 && bps < min_bps) bps = min_bps;
