@@ -438,6 +438,78 @@ def test_graph_replays_match_eager():
         _ = torch.randn(1000, device=DEV).sum().item()  # unrelated eager work between replays
 
 
+def _replay_check(fn, outs, tag):
+    """Capture fn() in a HIP graph on a side stream and replay it four times,
+    with unrelated eager work between replays; every replay must reproduce the
+    eager outputs bit for bit."""
+    torch.cuda.synchronize()
+    fn(None)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        fn(s.cuda_stream)  # warm-up on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn(s.cuda_stream)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, eager)):
+            assert torch.equal(a, b), f"{tag}: output {i} differs on replay {rep}"
+        _ = torch.randn(1000, device=DEV).sum().item()
+
+
+def test_graph_replays_cover_merges_caps_paging_and_prefill():
+    """Graph replays of decode layers whose splits merge in the kernel (the
+    arrival counters must be back at zero after each call) and in the merge
+    kernel, a capped KV-shared layer, the paged fused decode step, and a
+    prefill chunk."""
+    layers = [_desc(16, 8, 256, 100), _desc(16, 1, 512, 0, 1),
+              _desc(16, 8, 256, 100, owner=0, softcap=5.0)]
+    lens = [5, 333, 2049]
+    wl = _custom(layers, len(lens), "decode", kv_max=4096, seq_lens=lens, seed=31)
+    st = H.make_stack(wl, DEV)
+    H.fill_cache(st, wl, DEV)
+    bufs = H.StepBuffers(wl, DEV)
+    _replay_check(lambda sid: H.run_step(st, bufs, stream=sid), bufs.out, "decode")
+    for i in range(len(layers)):
+        q = f64(bufs.q[i])
+        ref = np.stack([oracle_decode(wl, i, b, q) for b in range(wl.batch)])
+        check_close(bufs.out[i], ref, f"graph decode layer {i}")
+    del st
+    # paged fused decode step: each replay writes the same token rows again
+    pst = H.make_paged_stack(wl, page_size=128, device=DEV, seed=8)
+    H.fill_cache(pst, wl, DEV)
+    gen = torch.Generator(device=DEV).manual_seed(9)
+    knew = [torch.randn((wl.batch, d.n_kv_heads, d.head_dim), generator=gen, device=DEV)
+            .to(torch.bfloat16) for d in layers[:2]]
+    vnew = [torch.randn((wl.batch, 8, 256), generator=gen, device=DEV).to(torch.bfloat16), None]
+
+    def fused(sid):
+        for i in range(2):
+            pst.decode_append(i, bufs.q[i], knew[i], vnew[i], bufs.lens, bufs.max_len,
+                              bufs.out[i], sid)
+        pst.decode(2, bufs.q[2], bufs.lens, bufs.max_len, bufs.out[2], sid)
+    _replay_check(fused, bufs.out, "paged fused decode")
+    del pst
+    torch.cuda.empty_cache()
+    # prefill chunk (sliding, global k_eq_v, capped shared)
+    wp = _custom(layers, 2, "prefill", kv_max=4096, start_pos=[0, 700], n_tok=64, seed=32)
+    sp = H.make_stack(wp, DEV)
+    H.fill_cache(sp, wp, DEV)
+    pb = H.StepBuffers(wp, DEV)
+    _replay_check(lambda sid: H.run_step(sp, pb, stream=sid), pb.out, "prefill")
+    for i in range(len(layers)):
+        q = f64(pb.q[i])
+        ref = np.stack([oracle_prefill(wp, i, b, q, tokens=range(0, 64, 9)) for b in range(2)])
+        check_close(f64(pb.out[i])[:, 0:64:9], ref, f"graph prefill layer {i}")
+
+
 # ---------------------------------------------------------------------------
 # robustness of the masking and of the online softmax
 # ---------------------------------------------------------------------------
