@@ -168,8 +168,9 @@ int32_t g4attn_append_kv(const g4attn_stack* stack, int32_t layer, const void* k
  *        A length <= 0 gives a zero output row.
  *   max_seq_len: host bound on seq_lens[b]; 1 <= max_seq_len <= kv_max.
  *   out: [batch][n_q_heads][head_dim] bf16.
- * Output = softmax(scale * q K^T over the visible keys) V, fp32 accumulation,
- * rounded to bf16 (round to nearest even).
+ * Output = softmax(s) V over the visible keys, s = scale * q K^T (each score
+ * replaced by softcap * tanh(s / softcap) when the layer sets a cap), fp32
+ * accumulation, rounded to bf16 (round to nearest even).
  * Errors: _NULL, _RANGE, _UNBOUND, _HIP.
  */
 int32_t g4attn_decode(const g4attn_stack* stack, int32_t layer, const void* q,
