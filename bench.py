@@ -432,6 +432,7 @@ def cpu_baseline(dec):
     gbs = nbytes / dt / 1e9
     log(f"[bench] cpu baseline {dt:.2f} s for {nbytes/1e9:.3f} GB -> {gbs:.3f} GB/s")
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "us_per_step": round(dt / CPU_REPS * 1e6, 1),
             "sample": f"{CPU_REPS} passes over one full step of the same workload (48 layers x "
                       f"16 sequences, {nbytes/CPU_REPS/1e9:.2f} GB of bf16 KV per pass), fp64 "
                       f"numpy oracle, compute timed {dt:.1f} s, BLAS threads limited to the "
