@@ -28,8 +28,8 @@ constexpr int kMaxDecodeSplits = 64;
 // Query rows (token x head pairs) per prefill workgroup.
 constexpr int kPrefillRows = 16;
 
-// keys per decode key block (both layer kinds)
-inline int decode_block(bool) { return 32; }
+// Keys per decode key block, on layers with and without a V plane.
+constexpr int kDecodeBlock = 32;
 
 // Waves per SIMD an attention kernel instance is built for: 2 (up to 256
 // registers per lane), or 1 where one wave needs more (head_dim 512 without

@@ -94,7 +94,10 @@ int32_t check_layer(const g4attn_stack* st, int32_t layer) {
 // A split also writes rows x head_dim fp32 partial outputs (and reads them
 // back in the merge); splits are made long enough that these stay within
 // an eighth of the split's cache bytes (this binds where many query heads
-// share one KV head, e.g. 16 rows over 16-key k_eq_v blocks).
+// share one KV head, e.g. 16 rows over the K-only blocks of k_eq_v layers).
+// A split also gets at least one block per wave where the context has them.
+// (Planning k_eq_v layers for more, shorter splits or fewer, longer ones
+// measured slower in both directions.)
 void decode_splits(int keys_max, int KB, int pairs, int rows, int planes,
                    int* blocks_per_split, int* n_splits) {
   const int nb_max = (keys_max + KB - 1) / KB + 1;  // +1: alignment of the first block
@@ -104,8 +107,9 @@ void decode_splits(int keys_max, int KB, int pairs, int rows, int planes,
   if (ns > nb_max) ns = nb_max;
   if (ns < 1) ns = 1;
   int bps = ceil_div(nb_max, ns);
-  // at least one block for each of a workgroup's 4 waves (short contexts,
-  // few sequences: fewer, fuller splits and a smaller merge)
+  // at least one block for each of a workgroup's 4 waves (short contexts over
+  // few sequences: fewer, fuller splits and a merge small enough to stay in
+  // the kernel)
   if (bps < 4) bps = nb_max < 4 ? nb_max : 4;
   // partial bytes per split: rows * D * 4; cache bytes per block: KB * D * 2 * planes
   const int min_bps = ceil_div(8 * rows * 4, KB * 2 * planes);
@@ -391,6 +395,15 @@ g4::PageTable page_table(const g4attn_stack* st, const int32_t* table) {
   return t;
 }
 
+// The current token's rows for a fused decode step: K always, V exactly when
+// the layer has a V plane.
+int32_t check_new_rows(const LayerPlan& p, const void* k_new, const void* v_new) {
+  if (!k_new) return fail(G4ATTN_ERR_NULL, "k_new must be non-NULL");
+  if (p.d.k_eq_v && v_new) return fail(G4ATTN_ERR_NULL, "v_new must be NULL on a k_eq_v layer");
+  if (!p.d.k_eq_v && !v_new) return fail(G4ATTN_ERR_NULL, "v_new must be non-NULL");
+  return G4ATTN_OK;
+}
+
 // The paged and unpaged entry points take the same arguments but for the
 // block table; each accepts only its own kind of stack.
 int32_t check_mode(const g4attn_stack* st, const int32_t* table, bool paged_call) {
@@ -485,7 +498,7 @@ int32_t decode_impl(const g4attn_stack* st, int32_t layer, const void* q, const 
   const int nh = G < 16 ? G : 16;
   const int keys_max = d.window > 0 && d.window < max_seq_len ? d.window : max_seq_len;
   g4::DecodeArgs a;
-  const int KB = g4::decode_block(d.k_eq_v != 0);
+  const int KB = g4::kDecodeBlock;
   decode_splits(keys_max, KB, batch * d.n_kv_heads * n_hblk, nh, d.k_eq_v ? 1 : 2,
                 &a.blocks_per_split, &a.n_splits);
   a.merge_in_kernel =
@@ -564,9 +577,7 @@ int32_t g4attn_decode_append(const g4attn_stack* st, int32_t layer, const void* 
   if (p.owner != layer)
     return fail(G4ATTN_ERR_SHARED_LAYER, "layer %d reads layer %d's cache and writes none", layer,
                 p.owner);
-  if (!k_new) return fail(G4ATTN_ERR_NULL, "k_new must be non-NULL");
-  if (p.d.k_eq_v && v_new) return fail(G4ATTN_ERR_NULL, "v_new must be NULL on a k_eq_v layer");
-  if (!p.d.k_eq_v && !v_new) return fail(G4ATTN_ERR_NULL, "v_new must be non-NULL");
+  if (int32_t rc = check_new_rows(p, k_new, v_new)) return rc;
   if (int32_t rc = check_mode(st, nullptr, false)) return rc;
   return decode_impl(st, layer, q, k_new, v_new, seq_lens, batch, max_seq_len, nullptr, out,
                      stream);
@@ -582,9 +593,7 @@ int32_t g4attn_decode_append_paged(const g4attn_stack* st, int32_t layer, const 
   if (p.owner != layer)
     return fail(G4ATTN_ERR_SHARED_LAYER, "layer %d reads layer %d's cache and writes none", layer,
                 p.owner);
-  if (!k_new) return fail(G4ATTN_ERR_NULL, "k_new must be non-NULL");
-  if (p.d.k_eq_v && v_new) return fail(G4ATTN_ERR_NULL, "v_new must be NULL on a k_eq_v layer");
-  if (!p.d.k_eq_v && !v_new) return fail(G4ATTN_ERR_NULL, "v_new must be non-NULL");
+  if (int32_t rc = check_new_rows(p, k_new, v_new)) return rc;
   return decode_impl(st, layer, q, k_new, v_new, seq_lens, batch, max_seq_len, block_table, out,
                      stream);
 }
