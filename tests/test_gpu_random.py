@@ -1,8 +1,9 @@
 """Seeded random GPU parity sweep: layer geometry, window, k_eq_v, logit cap,
 lengths (empty, single key, window and block edges, long) and the paged or
-unpaged cache are drawn at random for decode and prefill, and every output row
-is compared with the fp64 oracle to the same tolerance as the other parity
-tests.  The seed of each case is in its test id."""
+unpaged cache are drawn at random for decode, prefill and the fused decode
+step, and every output row is compared with the fp64 oracle to the same
+tolerance as the other parity tests.  The seed of each case is in its test
+id."""
 
 import math
 
@@ -89,3 +90,41 @@ def test_random_prefill_cases(seed):
     q = f64(bufs.q[0])
     ref = np.stack([oracle_prefill(wl, 0, b, q) for b in range(wl.batch)])
     check_close(bufs.out[0], ref, f"random prefill seed {seed}")
+
+
+@pytest.mark.parametrize("seed", list(range(3000, 3030)))
+def test_random_fused_decode_cases(seed):
+    """The fused decode step (append of the current token + decode, unpaged or
+    paged) on random layers: bit-identical to the unfused pair, outputs and
+    cache, and within tolerance of the oracle."""
+    r, desc, paged = _draw(seed)
+    kv_max = int(r.choice([128, 640, 2048]))
+    lens = [max(1, x) for x in _lens(r, kv_max, desc.window)]
+    say(f"[gpu] random fused seed={seed} {desc} paged={paged} kv_max={kv_max} lens={lens}")
+    wl = W.Workload("random fused", 9, [desc], len(lens), "decode", kv_max, 64, lens,
+                    seed_override=seed)
+    keqv = desc.k_eq_v
+    spans = [W.kv_span(wl, 0, b) for b in range(wl.batch)]
+    ks = [W.kv_rows(wl, 0, b, "k", DEV) for b in range(wl.batch)]
+    vs = None if keqv else [W.kv_rows(wl, 0, b, "v", DEV) for b in range(wl.batch)]
+    k_new = torch.stack([k[:, -1] for k in ks]).contiguous()
+    v_new = None if keqv else torch.stack([v[:, -1] for v in vs]).contiguous()
+    older = [(s, e - 1) for s, e in spans]
+    stacks = []
+    for _ in range(2):
+        st = _stack(wl, paged, seed)
+        H._append_span(st, 0, [k[:, :-1] for k in ks],
+                       None if keqv else [v[:, :-1] for v in vs], older, DEV)
+        stacks.append(st)
+    bufs = H.StepBuffers(wl, DEV)
+    fused = stacks[0].decode_append(0, bufs.q[0], k_new, v_new, bufs.lens, bufs.max_len)
+    pos = (bufs.lens - 1).to(torch.int32)
+    stacks[1].append_kv(0, k_new[:, None], None if keqv else v_new[:, None], pos,
+                        max_end_pos=bufs.max_len)
+    plain = stacks[1].decode(0, bufs.q[0], bufs.lens, bufs.max_len)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, plain)
+    assert torch.equal(stacks[0].cache, stacks[1].cache)
+    q = f64(bufs.q[0])
+    ref = np.stack([oracle_decode(wl, 0, b, q) for b in range(wl.batch)])
+    check_close(fused, ref, f"random fused seed {seed}")
