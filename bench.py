@@ -25,7 +25,7 @@ Also reported on the same line:
                 workload, on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-prefill] [--copy-calib]
+                       [--no-prefill] [--copy-calib] [--main-only] [--long-context-only]
 """
 
 from __future__ import annotations
@@ -448,6 +448,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one 1 GiB device copy, the reference for HBM byte counters")
+    ap.add_argument("--long-context-only", action="store_true",
+                    help="run only the long-context ragged decode stack and log its step time "
+                         "(no JSON line; for per-kernel profiles of that workload)")
     ap.add_argument("--main-only", action="store_true",
                     help="skip the TP=2 rank stack, the fused-append step and the paged step, "
                          "which launch the decode kernels at other shapes or in other "
@@ -468,6 +471,9 @@ def main():
         sys.exit(1)
     g4attn.load()
     stream = torch.cuda.Stream()
+    if args.long_context_only:
+        bench_long_decode(args, stream)
+        return
     if args.copy_calib:
         src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
