@@ -57,7 +57,7 @@ def _stack(wl, paged, seed):
 @pytest.mark.parametrize("seed", list(range(500, 560)))
 def test_random_decode_cases(seed):
     r, desc, paged = _draw(seed)
-    kv_max = int(r.choice([128, 640, 2048]))
+    kv_max = int(r.choice([100, 128, 640, 1000, 2048]))
     lens = _lens(r, kv_max, desc.window)
     say(f"[gpu] random decode seed={seed} {desc} paged={paged} kv_max={kv_max} lens={lens}")
     wl = W.Workload("random decode", 9, [desc], len(lens), "decode", kv_max, 64, lens,
@@ -75,7 +75,7 @@ def test_random_decode_cases(seed):
 @pytest.mark.parametrize("seed", list(range(2000, 2040)))
 def test_random_prefill_cases(seed):
     r, desc, paged = _draw(seed)
-    kv_max = int(r.choice([256, 1024]))
+    kv_max = int(r.choice([200, 256, 1000, 1024]))
     T = int(r.choice([1, 7, 16, 64]))
     starts = [int(r.integers(0, kv_max - T + 1)) for _ in range(int(r.integers(1, 4)))]
     say(f"[gpu] random prefill seed={seed} {desc} paged={paged} kv_max={kv_max} T={T} "
@@ -98,7 +98,7 @@ def test_random_fused_decode_cases(seed):
     paged) on random layers: bit-identical to the unfused pair, outputs and
     cache, and within tolerance of the oracle."""
     r, desc, paged = _draw(seed)
-    kv_max = int(r.choice([128, 640, 2048]))
+    kv_max = int(r.choice([100, 128, 640, 1000, 2048]))
     lens = [max(1, x) for x in _lens(r, kv_max, desc.window)]
     say(f"[gpu] random fused seed={seed} {desc} paged={paged} kv_max={kv_max} lens={lens}")
     wl = W.Workload("random fused", 9, [desc], len(lens), "decode", kv_max, 64, lens,
