@@ -100,6 +100,10 @@ struct DecodeArgs {
   float* part_ml;    // [B][n_q][n_splits][2]
   int32_t* counters; // [B][n_kv][n_hblk]
   int n_q, n_kv, G, n_hblk, cap, window, kv_max;
+  // host bound on seq_lens[b] (<= kv_max) that the split grid is planned
+  // from; longer lengths are clamped to it, so a violated bound changes the
+  // numbers but never the grid's coverage or the arrival counts
+  int max_len;
   // A sequence with nb key blocks uses ceil(nb / blocks_per_split) splits
   // (at most n_splits, the grid's x extent), so every split streams about
   // the same number of blocks whatever the sequence's length.
@@ -136,6 +140,7 @@ struct PrefillArgs {
   const int32_t* start_pos;
   uint16_t* out;  // [B][T][n_q][D]
   int batch, n_q, n_kv, G, T, cap, window, kv_max;
+  int max_start;  // host bound on start_pos[b]; larger starts are clamped to it
   // rows = T * G (token-major (token, head) pairs of one KV head), in
   // n_rowblk blocks of kPrefillRows
   int rows, n_rowblk;
@@ -153,7 +158,7 @@ struct MergeArgs {
   // splits in use per row follow from the sequence's length; rows of
   // sequences with at most one split were written by the decode kernel
   const int32_t* seq_lens;
-  int window, kv_max, KB, blocks_per_split;
+  int window, kv_max, max_len, KB, blocks_per_split;
 };
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s);

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(D / 4 > 64 ? D / 4 : 64) void merge_kernel(MergeArg
     if (row < (size_t)a.rows) {
       const int bseq = (int)(row / a.n_q);
       int L = a.seq_lens[bseq];
-      L = L < 0 ? 0 : (L > a.kv_max ? a.kv_max : L);
+      L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
       const int lo = a.window > 0 ? max(0, L - a.window) : 0;
       int f, e;
       decode_split_range(lo, L, a.KB, a.blocks_per_split, 0, &n_used, &f, &e);
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
     qrow = a.q + ((size_t)b * a.n_q + head0 + c16) * D;
     load_q();
     int L = a.seq_lens[b];
-    L = L < 0 ? 0 : (L > a.kv_max ? a.kv_max : L);
+    L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
     const int lo = a.window > 0 ? max(0, L - a.window) : 0;
     decode_split_range(lo, L, KB, a.blocks_per_split, split, &n_used, &blk_first, &blk_end);
     if (split > 0 && split >= n_used) return;  // nothing for this workgroup
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
     qrow = a.q + (((size_t)b * a.T + t_row) * a.n_q + g * a.G + h_row) * D;
     load_q();
     int start = a.start_pos[b];
-    start = start < 0 ? 0 : start;
+    start = start < 0 ? 0 : (start > a.max_start ? a.max_start : start);
     const int p_first = start + row0 / a.G;
     const int p_last = start + (row0 + nrows - 1) / a.G;
     const int p_row = start + t_row;

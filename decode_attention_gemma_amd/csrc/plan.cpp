@@ -520,6 +520,7 @@ int32_t decode_impl(const g4attn_stack* st, int32_t layer, const void* q, const 
   a.cap = p.cap;
   a.window = d.window;
   a.kv_max = st->kv_max;
+  a.max_len = max_seq_len;
   a.scale_log2 = d.scale * 1.4426950408889634f;
   a.softcap = d.softcap > 0.f ? 1 : 0;
   a.cap_in = a.softcap ? d.scale / d.softcap : 0.f;
@@ -539,6 +540,7 @@ int32_t decode_impl(const g4attn_stack* st, int32_t layer, const void* q, const 
     m.seq_lens = seq_lens;
     m.window = d.window;
     m.kv_max = st->kv_max;
+    m.max_len = max_seq_len;
     m.KB = KB;
     m.blocks_per_split = a.blocks_per_split;
     e = g4::launch_merge(m, static_cast<hipStream_t>(stream));
@@ -634,6 +636,7 @@ static int32_t prefill_impl(const g4attn_stack* st, int32_t layer, const void* q
   a.cap = p.cap;
   a.window = d.window;
   a.kv_max = st->kv_max;
+  a.max_start = max_start_pos;
   a.scale_log2 = d.scale * 1.4426950408889634f;
   a.softcap = d.softcap > 0.f ? 1 : 0;
   a.cap_in = a.softcap ? d.scale / d.softcap : 0.f;

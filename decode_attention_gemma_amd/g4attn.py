@@ -321,6 +321,10 @@ class Stack:
                                  device=self.device)
         self.workspace = torch.zeros(max(self.ws_nbytes, 256), dtype=torch.uint8,
                                      device=self.device)
+        # the zero fill runs on torch's current stream; the library's calls may
+        # go to any stream, so finish it before the first of them
+        if self.device.type == "cuda":
+            torch.cuda.synchronize(self.device)
         g4attn_bind(self.handle, self.cache, self.workspace)
 
     def close(self):

@@ -31,9 +31,11 @@
  *     They allocate nothing, so they may be captured into a HIP graph.
  *   - Tensors are dense, row-major, bf16 (IEEE binary32's upper 16 bits), and
  *     16-byte aligned.  Length / position arrays are int32 on the device.
- *   - Device length arrays must respect the host-side hints passed with them;
- *     kernels clamp every cache access into the cache, so a violation gives
- *     wrong numbers, never an out-of-bounds access.
+ *   - Device length arrays must respect the host-side hints passed with them.
+ *     The kernels clamp each length or start position to its hint (and every
+ *     cache access into the cache), so a violation gives wrong numbers for
+ *     that sequence, never an out-of-bounds access, and leaves no state that
+ *     affects later calls.
  *   - Calls that use one stack's workspace (decode, prefill) must be ordered
  *     on one stream; calls on different streams that touch disjoint cache
  *     regions and different workspaces are safe.
@@ -94,7 +96,9 @@ typedef struct g4attn_layer_desc {
 typedef struct g4attn_stack g4attn_stack; /* opaque, host-side plan */
 
 /*
- * Validate the descriptors, resolve owners and plan the cache.  Host only; no
+ * Validate the descriptors, resolve owners ([FR] 2.1: a KV-shared layer names
+ * an earlier owning layer) and plan the one resident cache ([FR] 5: a fixed
+ * buffer on the device, sized once for the largest context).  Host only; no
  * HIP call.  max_batch: sequences per call; kv_max: positions per sequence
  * (every position < kv_max); max_chunk: new tokens per append/prefill call.
  * Errors: G4ATTN_ERR_NULL, _DESC, _OWNER, _UNSUPPORTED.  *out is set only on
@@ -125,21 +129,31 @@ void g4attn_stack_destroy(g4attn_stack* stack);
 int32_t g4attn_cache_bytes(const g4attn_stack* stack, uint64_t* bytes);
 int32_t g4attn_workspace_bytes(const g4attn_stack* stack, uint64_t* bytes);
 
-/* Attach caller-owned device buffers (256-byte aligned).  Host only.
+/* Attach caller-owned device buffers (256-byte aligned): the resident cache
+ * that every prefill and decode call of the stack reads and appends write
+ * ([FR] 5: one device buffer filled by the prefill graph and read by the
+ * decode graph, never copied back to the host) and the workspace.  Host only.
  * Errors: G4ATTN_ERR_NULL, G4ATTN_ERR_RANGE (misaligned). */
 int32_t g4attn_bind(g4attn_stack* stack, void* cache, void* workspace);
 
 /* Host-side lookups, bit-exact with what the kernels do (test hooks). */
 /* Layer whose cache `layer` reads ([FR] 2.1). */
 int32_t g4attn_resolve_owner(const g4attn_stack* stack, int32_t layer, int32_t* owner);
-/* Slots per (sequence, KV head) of the cache `layer` reads. */
+/* Slots per (sequence, KV head) of the cache `layer` reads: the full context
+ * on global layers, a window-plus-chunk ring on sliding ones ([FR]
+ * introduction table: sliding windows of 512 / 1024 positions; [12B] "Why
+ * this is its own port": window 1024). */
 int32_t g4attn_layer_capacity(const g4attn_stack* stack, int32_t layer, int32_t* cap);
-/* Keys [lo, hi) visible to a query at q_pos when n_keys positions exist. */
+/* Keys [lo, hi) visible to a query at q_pos when n_keys positions exist:
+ * hi = min(q_pos + 1, n_keys) (causal); lo = max(0, q_pos - window + 1) on a
+ * sliding layer, else 0 ([FR] introduction table: sliding vs global layers
+ * and their windows). */
 int32_t g4attn_key_range(const g4attn_stack* stack, int32_t layer, int64_t q_pos,
                          int64_t n_keys, int64_t* lo, int64_t* hi);
 /* Byte offsets in the cache of element d of the K row and of the V row
- * (== the K element when k_eq_v) of (sequence b, KV head, position pos) read
- * by `layer`.  Errors: _NULL, _RANGE. */
+ * (== the K element when k_eq_v, [12B] "Why this is its own port": K reused
+ * as V) of (sequence b, KV head, position pos) read by `layer` (the owner's
+ * planes, [FR] 2.1).  Errors: _NULL, _RANGE, _UNSUPPORTED (paged stack). */
 int32_t g4attn_kv_offset(const g4attn_stack* stack, int32_t layer, int32_t b, int32_t kv_head,
                          int64_t pos, int32_t d, int64_t* off_k, int64_t* off_v);
 
@@ -166,7 +180,9 @@ int32_t g4attn_append_kv(const g4attn_stack* stack, int32_t layer, const void* k
  *   seq_lens: int32[batch], keys cached for each sequence INCLUDING the
  *        current token (already appended); the query sits at seq_lens[b]-1.
  *        A length <= 0 gives a zero output row.
- *   max_seq_len: host bound on seq_lens[b]; 1 <= max_seq_len <= kv_max.
+ *   max_seq_len: host bound on seq_lens[b]; 1 <= max_seq_len <= kv_max.  The
+ *        key splits are planned from it; a larger seq_lens[b] is treated as
+ *        max_seq_len.
  *   out: [batch][n_q_heads][head_dim] bf16.
  * Output = softmax(s) V over the visible keys, s = scale * q K^T (each score
  * replaced by softcap * tanh(s / softcap) when the layer sets a cap), fp32
@@ -202,6 +218,7 @@ int32_t g4attn_decode_append(const g4attn_stack* stack, int32_t layer, const voi
  *   start_pos: int32[batch]; token t of sequence b sits at start_pos[b] + t.
  *        The chunk's own K/V must already be appended (to the owning layer).
  *   max_start_pos: host bound on start_pos[b]; max_start_pos + n_tok <= kv_max.
+ *        A larger start_pos[b] is treated as max_start_pos.
  *   out: [batch][n_tok][n_q_heads][head_dim] bf16.
  * Errors: _NULL, _RANGE (n_tok > max_chunk, ...), _UNBOUND, _HIP.
  */

@@ -2,10 +2,14 @@
 
 Tolerance for floating point (bf16 output of fp32-accumulated attention on
 bf16-rounded inputs), per layer:
-  * max over elements of (|gpu - oracle| - u/2) <= 1e-2, where u/2 is half a
+  * max |gpu - oracle| <= 1e-2 over every output whose oracle value is below 2
+    in magnitude (there half a bf16 unit in the last place is at most 2^-8, so
+    the bar is the plain one);
+  * over all outputs, max (|gpu - oracle| - u/2) <= 1e-2, where u/2 is half a
     bf16 unit in the last place of the oracle value: the error beyond the
     rounding of the result to the bf16 output type, which no bf16-output kernel
-    can avoid (an output of 4.3246 must become 4.3125 or 4.3438);
+    can avoid (an output of 4.3246 must become 4.3125 or 4.3438, 1.2e-2 away
+    or more);
   * ||gpu - oracle||_2 / ||oracle||_2 <= 5e-3.
 Index work (owner / key-range resolution, cache offsets) is compared
 bit-exactly; a single visible key must return its value row bit-exactly (its
@@ -63,11 +67,14 @@ def check_close(got, ref, tag):
     assert np.isfinite(g).all(), f"{tag}: non-finite output"
     d = np.abs(g - ref)
     max_abs = float(d.max()) if d.size else 0.0
+    small = np.abs(ref) < 2.0
+    max_abs_small = float(d[small].max()) if small.any() else 0.0
     excess = float(np.maximum(d - bf16_half_ulp(ref), 0.0).max()) if d.size else 0.0
     nref = float(np.linalg.norm(ref))
     rel = float(np.linalg.norm(g - ref)) / nref if nref > 0 else float(np.linalg.norm(g - ref))
-    assert excess <= MAX_ABS and rel <= REL_L2, (
-        f"{tag}: max_abs {max_abs:.3e} (beyond output rounding {excess:.3e}) rel_l2 {rel:.3e}")
+    assert max_abs_small <= MAX_ABS and excess <= MAX_ABS and rel <= REL_L2, (
+        f"{tag}: max_abs {max_abs:.3e} (|oracle| < 2: {max_abs_small:.3e}; beyond output "
+        f"rounding {excess:.3e}) rel_l2 {rel:.3e}")
     return max_abs, rel
 
 
@@ -788,3 +795,33 @@ def test_paged_ragged_lengths_against_oracle():
         q = f64(bufs.q[i])
         ref = np.stack([oracle_decode(wl, i, b, q) for b in range(wl.batch)])
         check_close(bufs.out[i], ref, f"paged ragged layer {i}")
+
+
+def test_length_beyond_hint_is_clamped_and_leaves_no_state():
+    """seq_lens above the max_seq_len hint: the kernels treat them as the hint,
+    so the call covers only the planned splits, every arrival counter returns
+    to zero, and the next valid call is exact.  Layers: a sliding layer whose
+    splits merge in the kernel and a global k_eq_v layer whose splits go to the
+    merge kernel."""
+    layers = [_desc(16, 8, 256, 1024), _desc(16, 1, 512, 0, 1)]
+    wl = W.Workload("hint violation", 90, layers, batch=4, kind="decode", kv_max=8192,
+                    seq_lens=[8000, 3000, 100, 2500])
+    st, bufs = run_workload(wl)
+    n_ctr = max(wl.batch * d.n_kv_heads * ((d.n_q_heads // d.n_kv_heads + 15) // 16)
+                for d in layers)
+    for layer in range(wl.n_layers):
+        q = f64(bufs.q[layer])
+        ref = np.stack([oracle_decode(wl, layer, b, q) for b in range(wl.batch)])
+        for hint in (64, 100, 1000):
+            bad = torch.empty_like(bufs.q[layer])
+            say(f"[gpu] layer {layer}: lengths {wl.seq_lens} under hint {hint}")
+            st.decode(layer, bufs.q[layer], bufs.lens, hint, bad)
+            torch.cuda.synchronize()
+            assert np.isfinite(f64(bad)).all()
+            ctr = st.workspace[: 4 * n_ctr].view(torch.int32)
+            assert int(ctr.abs().sum()) == 0, f"counters left at {ctr.tolist()}"
+            good = torch.full_like(bufs.q[layer], float("nan"))
+            st.decode(layer, bufs.q[layer], bufs.lens, bufs.max_len, good)
+            torch.cuda.synchronize()
+            check_close(good, ref, f"layer {layer} after a hint-{hint} call")
+            assert int(st.workspace[: 4 * n_ctr].view(torch.int32).abs().sum()) == 0
