@@ -161,6 +161,15 @@ struct MergeArgs {
   int window, kv_max, max_len, KB, blocks_per_split;
 };
 
+// Library-owned decode scratch (allocation-free decode): kScratchBytes per
+// GPU, the first kScratchCounterBytes of it arrival counters.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr size_t kScratchCounterBytes = size_t(256) << 10;
+// Device address of the current GPU's scratch; *first_use is set on the
+// first lookup on that GPU (its counters must then be zeroed once).
+hipError_t scratch_address(void** ptr, bool* first_use);
+hipError_t launch_zero(int32_t* p, int n, hipStream_t s);
+
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s);
 hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, int batch, hipStream_t s);
 hipError_t launch_prefill(int head_dim, bool k_eq_v, const PrefillArgs& a, hipStream_t s);

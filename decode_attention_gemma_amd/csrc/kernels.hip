@@ -25,6 +25,7 @@
 #include <stdint.h>
 
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "internal.h"
@@ -1017,6 +1018,53 @@ hipError_t prefill_launch(const PrefillArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// library-owned decode scratch (the allocation-free decode entry point)
+// ---------------------------------------------------------------------------
+//
+// Split partials and arrival counters of g4attn_decode_noalloc live here
+// instead of in a caller-bound workspace.  Each GPU the library runs on holds
+// its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels get the device address that
+// hipGetSymbolAddress returns for the current device.
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ __launch_bounds__(256) void zero_kernel(int32_t* p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+hipError_t scratch_address(void** ptr, bool* first_use) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  *first_use = g_scratch_ptr[dev] == nullptr;
+  if (*first_use) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_zero(int32_t* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s) {
   dim3 grid(a.n_new * a.n_kv, batch);

@@ -479,16 +479,20 @@ int32_t g4attn_append_kv_paged(const g4attn_stack* st, int32_t layer, const void
 namespace {
 
 // Decode, optionally writing the current token's K / V rows first (k_new).
+// use_scratch: split partials and counters go to the library's own device
+// scratch instead of the bound workspace (nothing is allocated either way).
 int32_t decode_impl(const g4attn_stack* st, int32_t layer, const void* q, const void* k_new,
                     const void* v_new, const int32_t* seq_lens, int32_t batch,
-                    int32_t max_seq_len, const int32_t* table, void* out, void* stream) {
+                    int32_t max_seq_len, const int32_t* table, void* out, void* stream,
+                    bool use_scratch = false) {
   if (!q || !seq_lens || !out) return fail(G4ATTN_ERR_NULL, "q, seq_lens and out must be non-NULL");
   if (batch <= 0 || batch > st->max_batch)
     return fail(G4ATTN_ERR_RANGE, "batch %d not in [1, %d]", batch, st->max_batch);
   if (max_seq_len < 1 || max_seq_len > st->kv_max)
     return fail(G4ATTN_ERR_RANGE, "max_seq_len %d not in [1, kv_max=%d]", max_seq_len,
                 st->kv_max);
-  if (!st->cache || !st->ws) return fail(G4ATTN_ERR_UNBOUND, "cache/workspace not bound");
+  if (use_scratch ? !st->cache : (!st->cache || !st->ws))
+    return fail(G4ATTN_ERR_UNBOUND, use_scratch ? "cache not bound" : "cache/workspace not bound");
   const LayerPlan& p = st->L[layer];
   const g4attn_layer_desc& d = p.d;
   const int G = d.n_q_heads / d.n_kv_heads;
@@ -510,9 +514,41 @@ int32_t decode_impl(const g4attn_stack* st, int32_t layer, const void* q, const 
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.seq_lens = seq_lens;
   a.out = static_cast<uint16_t*>(out);
-  a.counters = reinterpret_cast<int32_t*>(st->ws + st->ws_ctr_off);
-  a.part_ml = reinterpret_cast<float*>(st->ws + st->ws_ml_off);
-  a.part_o = reinterpret_cast<float*>(st->ws + st->ws_o_off);
+  if (use_scratch) {
+    // counters first, then (m, l) pairs and partial outputs sized for this
+    // call's split plan (a single split writes its output directly and
+    // touches neither)
+    const uint64_t n_ctr = a.n_splits > 1 ? (uint64_t)batch * d.n_kv_heads * n_hblk : 0;
+    const uint64_t rows = a.n_splits > 1 ? (uint64_t)batch * d.n_q_heads * a.n_splits : 0;
+    const uint64_t ml_bytes = align256(rows * 2 * 4);
+    const uint64_t need = g4::kScratchCounterBytes + ml_bytes + rows * d.head_dim * 4;
+    if (n_ctr * 4 > g4::kScratchCounterBytes || need > g4::kScratchBytes)
+      return fail(G4ATTN_ERR_UNSUPPORTED,
+                  "layer %d: this call needs %llu bytes of decode scratch (%llu counters); the "
+                  "library holds %llu bytes (%llu counters) per GPU",
+                  layer, (unsigned long long)need, (unsigned long long)n_ctr,
+                  (unsigned long long)g4::kScratchBytes,
+                  (unsigned long long)(g4::kScratchCounterBytes / 4));
+    void* base = nullptr;
+    bool first = false;
+    hipError_t e = g4::scratch_address(&base, &first);
+    if (e != hipSuccess)
+      return fail(G4ATTN_ERR_HIP, "decode scratch address: %s", hipGetErrorString(e));
+    char* sc = static_cast<char*>(base);
+    if (first) {  // the kernels leave the counters at zero after every call
+      e = g4::launch_zero(reinterpret_cast<int32_t*>(sc), (int)(g4::kScratchCounterBytes / 4),
+                          static_cast<hipStream_t>(stream));
+      if (e != hipSuccess)
+        return fail(G4ATTN_ERR_HIP, "decode scratch clear: %s", hipGetErrorString(e));
+    }
+    a.counters = reinterpret_cast<int32_t*>(sc);
+    a.part_ml = reinterpret_cast<float*>(sc + g4::kScratchCounterBytes);
+    a.part_o = reinterpret_cast<float*>(sc + g4::kScratchCounterBytes + ml_bytes);
+  } else {
+    a.counters = reinterpret_cast<int32_t*>(st->ws + st->ws_ctr_off);
+    a.part_ml = reinterpret_cast<float*>(st->ws + st->ws_ml_off);
+    a.part_o = reinterpret_cast<float*>(st->ws + st->ws_o_off);
+  }
   a.n_q = d.n_q_heads;
   a.n_kv = d.n_kv_heads;
   a.G = G;
@@ -560,6 +596,15 @@ int32_t g4attn_decode(const g4attn_stack* st, int32_t layer, const void* q,
   if (int32_t rc = check_mode(st, nullptr, false)) return rc;
   return decode_impl(st, layer, q, nullptr, nullptr, seq_lens, batch, max_seq_len, nullptr, out,
                      stream);
+}
+
+int32_t g4attn_decode_noalloc(const g4attn_stack* st, int32_t layer, const void* q,
+                              const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                              void* out, void* stream) {
+  if (int32_t rc = check_layer(st, layer)) return rc;
+  if (int32_t rc = check_mode(st, nullptr, false)) return rc;
+  return decode_impl(st, layer, q, nullptr, nullptr, seq_lens, batch, max_seq_len, nullptr, out,
+                     stream, true);
 }
 
 int32_t g4attn_decode_paged(const g4attn_stack* st, int32_t layer, const void* q,

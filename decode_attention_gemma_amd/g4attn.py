@@ -59,6 +59,8 @@ _SIGNATURES = {
                                    c_int32, c_int32, c_int32, c_void_p]),
     "g4attn_decode": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32,
                                 c_void_p, c_void_p]),
+    "g4attn_decode_noalloc": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32,
+                                        c_void_p, c_void_p]),
     "g4attn_decode_append": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "g4attn_prefill": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32,
@@ -224,6 +226,12 @@ def g4attn_decode(stack: int, layer: int, q, seq_lens, batch: int, max_seq_len: 
                   stream=None) -> None:
     _check(load().g4attn_decode(stack, layer, _ptr(q), _ptr(seq_lens), batch, max_seq_len,
                                 _ptr(out), _stream(stream)))
+
+
+def g4attn_decode_noalloc(stack: int, layer: int, q, seq_lens, batch: int, max_seq_len: int,
+                          out, stream=None) -> None:
+    _check(load().g4attn_decode_noalloc(stack, layer, _ptr(q), _ptr(seq_lens), batch,
+                                        max_seq_len, _ptr(out), _stream(stream)))
 
 
 def g4attn_decode_append(stack: int, layer: int, q, k_new, v_new, seq_lens, batch: int,

@@ -194,6 +194,27 @@ int32_t g4attn_decode(const g4attn_stack* stack, int32_t layer, const void* q,
                       void* stream);
 
 /*
+ * g4attn_decode for callers that cannot allocate device memory or use a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, results and errors as
+ * g4attn_decode on an unpaged stack whose cache is bound; the bound workspace
+ * is not touched.  The split partials and arrival counters live instead in a
+ * scratch array the library holds on each GPU it runs on (16 MiB, of which
+ * 256 KiB are counters; kept until the process ends).  A call whose split
+ * plan needs more (about batch x n_q_heads x splits x (head_dim + 2) x 4
+ * bytes, or more than 65536 (sequence, KV head, head block) counters) returns
+ * G4ATTN_ERR_UNSUPPORTED before any launch.  No hipMalloc or other
+ * allocation happens in this call; its first call on a GPU looks up that
+ * GPU's scratch address and clears the counters with one small kernel on
+ * `stream`.  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap in time on one GPU (different streams, or several host threads)
+ * race and must be ordered by the caller.
+ */
+int32_t g4attn_decode_noalloc(const g4attn_stack* stack, int32_t layer, const void* q,
+                              const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                              void* out, void* stream);
+
+/*
  * Decode step with the current token's K/V write fused in ([FR] 4 and 5: the
  * decode graph writes the new token's K/V into the resident cache in place
  * and attends over it).  Same as g4attn_append_kv of one token at position
