@@ -58,28 +58,48 @@ def kv_bytes(wl, layer):
 
 
 DOMINANT_KERNEL = "attend_kernel<256, false, 4, false, false, false>"
+PREFILL_KERNEL = "attend_kernel<512, true, 8, true, false, false>"
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "attend_12b_hbm_bytes.md")
 KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_gemma_amd", "csrc", "kernels.hip")
+PLAN_SOURCE = os.path.join(ROOT, "decode_attention_gemma_amd", "csrc", "plan.cpp")
+
+
+def source_hashes():
+    """sha256[:16] of the kernel source and of the host plan (split planning
+    and launch shapes), the two files a kernel's counters depend on."""
+    import hashlib
+
+    return {os.path.basename(f): hashlib.sha256(open(f, "rb").read()).hexdigest()[:16]
+            for f in (KERNEL_SOURCE, PLAN_SOURCE)}
 
 
 def counter_traffic(kernel: str):
     """HBM bytes per launch of `kernel` (calibrated FETCH_SIZE + WRITE_SIZE)
     from the committed rocprofv3 summary, or None when that summary was taken
-    on a different kernel source than the one built now."""
-    import hashlib
-
+    on a different kernel source or host plan than the one built now."""
     try:
         text = open(COUNTER_SUMMARY).read()
-        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+        hashes = source_hashes()
     except OSError:
         return None
-    if f"kernels.hip sha256[:16]: {src}" not in text:
+    if any(f"{name} sha256[:16]: {h}" not in text for name, h in hashes.items()):
         return None
     for row in text.splitlines():
         cells = [c.strip() for c in row.strip().strip("|").split("|")]
         if len(cells) == 6 and cells[0] == kernel:
             return int(round((float(cells[3]) + float(cells[5])) * 1e6))
     return None
+
+
+def prefill_kv_bytes(wl, layer):
+    """Unique K and V bytes a prefill call of `layer` reads: every key some
+    token of the chunk sees, once (V only where the layer has a V plane)."""
+    d = wl.layers[layer]
+    keys = 0
+    for s in wl.start_pos:
+        lo = max(0, s - d.window + 1) if d.window > 0 else 0
+        keys += s + wl.n_tok - lo
+    return keys * d.n_kv_heads * d.head_dim * 2 * (1 if d.k_eq_v else 2)
 
 
 def prefill_flops(wl, layer):
@@ -106,22 +126,30 @@ def graph_of(fn, stream):
     return g
 
 
-def time_graph(g, warmup, reps):
-    """Mean ms per replay; replays run on the current stream, where the
-    events are recorded too."""
+def time_graph(g, warmup, reps, stats=None):
+    """Median ms per replay over `reps` timed replays.  Replays run on the
+    current stream, where a HIP event is recorded between consecutive
+    replays; the timed region is bracketed by device synchronizations.  When
+    `stats` is a dict it also receives the mean over the whole region."""
+    import statistics
+
     import torch
 
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
     cur = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(cur)
-    for _ in range(reps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(cur)
+    for i in range(reps):
         g.replay()
-    e1.record(cur)
+        ev[i + 1].record(cur)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    if stats is not None:
+        stats["mean_ms"] = ev[0].elapsed_time(ev[reps]) / reps
+        stats["reps"] = reps
+    return statistics.median(per)
 
 
 def bench_decode(args, stream):
@@ -137,7 +165,8 @@ def bench_decode(args, stream):
     step_graph = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream), stream)
     log(f"[bench] decode step: {args.warmup} warm-up, {args.steps} timed replays")
     t0 = time.perf_counter()
-    ms = time_graph(step_graph, args.warmup, args.steps)
+    stats = {}
+    ms = time_graph(step_graph, args.warmup, args.steps, stats)
     wall = time.perf_counter() - t0
     step_bytes = sum(kv_bytes(wl, i) for i in range(wl.n_layers))
     gbs = step_bytes / (ms * 1e-3) / 1e9
@@ -148,18 +177,19 @@ def bench_decode(args, stream):
     sliding = [i for i in range(wl.n_layers) if wl.layers[i].window > 0]
     dom_graph = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream, layers=sliding),
                          stream)
-    dom_ms = time_graph(dom_graph, 3, max(args.steps, 10)) / len(sliding)
+    dom_ms = time_graph(dom_graph, 3, max(args.steps, 20)) / len(sliding)
     dom_bytes = kv_bytes(wl, sliding[0])
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     log(f"[bench] sliding decode kernel {dom_ms*1e3:.1f} us/launch, {dom_gbs:.0f} GB/s")
     glob = [i for i in range(wl.n_layers) if wl.layers[i].window == 0]
     glob_graph = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream, layers=glob),
                           stream)
-    glob_ms = time_graph(glob_graph, 3, max(args.steps, 10)) / len(glob)
+    glob_ms = time_graph(glob_graph, 3, max(args.steps, 20)) / len(glob)
     glob_gbs = kv_bytes(wl, glob[0]) / (glob_ms * 1e-3) / 1e9
     log(f"[bench] global decode kernel {glob_ms*1e3:.1f} us/launch, {glob_gbs:.0f} GB/s")
     out = {
-        "wl": wl, "st": st, "bufs": bufs, "ms": ms, "step_bytes": step_bytes, "gbs": gbs,
+        "wl": wl, "st": st, "bufs": bufs, "ms": ms, "mean_ms": stats["mean_ms"],
+        "step_bytes": step_bytes, "gbs": gbs,
         "dom": {"ms": dom_ms, "bytes": dom_bytes, "gbs": dom_gbs},
         "glob": {"ms": glob_ms, "bytes": kv_bytes(wl, glob[0]), "gbs": glob_gbs},
     }
@@ -371,27 +401,47 @@ def bench_prefill(prefix, args, stream):
     flops = sum(prefill_flops(wl, i) for i in range(wl.n_layers))
     tf = flops / (ms * 1e-3) / 1e12
     glob = [i for i in range(wl.n_layers) if wl.layers[i].window == 0]
+    slid = [i for i in range(wl.n_layers) if wl.layers[i].window > 0]
     gg = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream, layers=glob), stream)
-    gms = time_graph(gg, 2, max(args.steps, 5)) / len(glob)
+    gms = time_graph(gg, 2, max(args.steps, 20)) / len(glob)
+    sg = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream, layers=slid), stream)
+    sms = time_graph(sg, 2, max(args.steps, 20)) / len(slid)
     gtf = prefill_flops(wl, glob[0]) / (gms * 1e-3) / 1e12
+    stf = prefill_flops(wl, slid[0]) / (sms * 1e-3) / 1e12
+    sgbs = prefill_kv_bytes(wl, slid[0]) / (sms * 1e-3) / 1e9
     log(f"[bench] prefill P={prefix}: {ms*1e3:.1f} us/step, {tf:.1f} TFLOP/s; "
-        f"global layer {gms*1e3:.1f} us, {gtf:.1f} TFLOP/s")
-    del st, bufs, g, gg
+        f"global layer {gms*1e3:.1f} us, {gtf:.1f} TFLOP/s; sliding layer {sms*1e3:.1f} us, "
+        f"{stf:.1f} TFLOP/s, {sgbs:.0f} GB/s of unique KV")
+    del st, bufs, g, gg, sg
     torch.cuda.empty_cache()
     return {"us_per_step": round(ms * 1e3, 2), "tflops": round(tf, 2),
             "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4), "gflop_per_step": round(flops / 1e9, 2),
-            "global_layer_us": round(gms * 1e3, 2), "global_layer_tflops": round(gtf, 2)}
+            "global_layer_us": round(gms * 1e3, 2), "global_layer_tflops": round(gtf, 2),
+            "global_layer_gflop": round(prefill_flops(wl, glob[0]) / 1e9, 3),
+            "sliding_layer_us": round(sms * 1e3, 2), "sliding_layer_tflops": round(stf, 2),
+            "sliding_layer_kv_gbs": round(sgbs, 1)}
 
 
-CPU_REPS = 8  # oracle passes over each layer: about 10 s of compute on 16 cores
+CPU_REPS = 4  # oracle passes over the decode step: about 5 s of compute on 16 cores
 
 
-def cpu_baseline(dec):
-    """The fp64 oracle on the same decode workload, layer by layer (inputs are
-    copied to the host and widened to fp64 outside the timed region); each
-    layer's computation is repeated CPU_REPS times so the timed sample is
-    several seconds long."""
-    import numpy as np
+def _host64(t):
+    import torch
+
+    return t.to("cpu", torch.float64).numpy()
+
+
+def cpu_baseline(dec, gpu_prefill_tflops=None, gpu_long_gbs=None):
+    """The fp64 oracle, timed on the host cores on bounded samples of the
+    benchmarked workloads (inputs are the same seeded bf16 tensors, copied to
+    the host and widened to fp64 outside the timed regions):
+      decode   every layer and sequence of the 12B decode step, CPU_REPS passes;
+      prefill  the 64-token chunk at prefix 4032: its first 12 layers (10
+               sliding, 2 global) for all 4 sequences (flops counted as the
+               metric's visible pairs);
+      long     the long-context ragged stack: one sliding and one global owner
+               layer for all 64 sequences."""
+    import numpy as np  # noqa: F401
     import torch
 
     from decode_attention_gemma_amd import workloads as W
@@ -411,12 +461,12 @@ def cpu_baseline(dec):
     for layer in range(wl.n_layers):
         d = wl.layers[layer]
         o = wl.owner(layer)
-        q = bufs.q[layer].to("cpu", torch.float64).numpy()
+        q = _host64(bufs.q[layer])
         inputs = []
         for b in range(wl.batch):
             pos0, _ = W.kv_span(wl, o, b)
-            K = W.kv_rows(wl, o, b, "k", "cuda").to("cpu", torch.float64).numpy()
-            V = None if d.k_eq_v else W.kv_rows(wl, o, b, "v", "cuda").to("cpu", torch.float64).numpy()
+            K = _host64(W.kv_rows(wl, o, b, "k", "cuda"))
+            V = None if d.k_eq_v else _host64(W.kv_rows(wl, o, b, "v", "cuda"))
             inputs.append((q[b], K, V, wl.seq_lens[b], pos0))
             L = wl.seq_lens[b]
             keys = min(L, d.window) if d.window > 0 else L
@@ -427,22 +477,77 @@ def cpu_baseline(dec):
                 O.decode_sequence(d, qb, K, V, L, k_pos0=pos0)
         dt += time.perf_counter() - t0
         del inputs
+    gbs = nbytes / dt / 1e9
+    log(f"[bench] cpu baseline decode {dt:.2f} s for {nbytes/1e9:.3f} GB -> {gbs:.3f} GB/s")
+
+    # prefill chunk, prefix 4032: the first 12 layers (10 sliding, 2 global),
+    # all 4 sequences
+    pw = W.g12b_prefill(4032)
+    p_dt, p_flops = 0.0, 0
+    for layer in range(12):
+        d = pw.layers[layer]
+        q = _host64(W.q_tensor(pw, layer, "cuda"))
+        for b in range(pw.batch):
+            pos0, _ = W.kv_span(pw, layer, b)
+            K = _host64(W.kv_rows(pw, layer, b, "k", "cuda"))
+            V = None if d.k_eq_v else _host64(W.kv_rows(pw, layer, b, "v", "cuda"))
+            t0 = time.perf_counter()
+            O.prefill_sequence(d, q[b], K, V, pw.start_pos[b], k_pos0=pos0)
+            p_dt += time.perf_counter() - t0
+        p_flops += prefill_flops(pw, layer)
+    p_gfs = p_flops / p_dt / 1e9
+    log(f"[bench] cpu baseline prefill {p_dt:.2f} s for {p_flops/1e9:.2f} GFLOP -> "
+        f"{p_gfs:.3f} GFLOP/s")
+
+    # long-context ragged decode: one sliding and one global owner layer, all
+    # 64 sequences
+    lw = W.long_decode()
+    l_dt, l_bytes = 0.0, 0
+    for layer in (0, 5):
+        d = lw.layers[layer]
+        q = _host64(W.q_tensor(lw, layer, "cuda"))
+        for b in range(lw.batch):
+            pos0, _ = W.kv_span(lw, layer, b)
+            K = _host64(W.kv_rows(lw, layer, b, "k", "cuda"))
+            V = None if d.k_eq_v else _host64(W.kv_rows(lw, layer, b, "v", "cuda"))
+            t0 = time.perf_counter()
+            O.decode_sequence(d, q[b], K, V, lw.seq_lens[b], k_pos0=pos0)
+            l_dt += time.perf_counter() - t0
+            L = lw.seq_lens[b]
+            keys = min(L, d.window) if d.window > 0 else L
+            l_bytes += keys * d.n_kv_heads * d.head_dim * 2 * (1 if d.k_eq_v else 2)
+            del K, V
+    l_gbs = l_bytes / l_dt / 1e9
+    log(f"[bench] cpu baseline long-context decode {l_dt:.2f} s for {l_bytes/1e9:.3f} GB -> "
+        f"{l_gbs:.3f} GB/s")
     if ctx is not None:
         ctx.restore_original_limits()
-    gbs = nbytes / dt / 1e9
-    log(f"[bench] cpu baseline {dt:.2f} s for {nbytes/1e9:.3f} GB -> {gbs:.3f} GB/s")
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "us_per_step": round(dt / CPU_REPS * 1e6, 1),
-            "sample": f"{CPU_REPS} passes over one full step of the same workload (48 layers x "
-                      f"16 sequences, {nbytes/CPU_REPS/1e9:.2f} GB of bf16 KV per pass), fp64 "
-                      f"numpy oracle, compute timed {dt:.1f} s, BLAS threads limited to the "
-                      f"{cores} cores"}
+            "sample": f"{CPU_REPS} passes over one full step of the same decode workload (48 "
+                      f"layers x 16 sequences, {nbytes/CPU_REPS/1e9:.2f} GB of bf16 KV per "
+                      f"pass), fp64 numpy oracle, compute timed {dt:.1f} s, BLAS threads "
+                      f"limited to the {cores} cores",
+            "prefill": {"value": round(p_gfs, 3), "unit": "GFLOP/s", "kind": "oracle",
+                        "seconds": round(p_dt, 2),
+                        "gpu_over_oracle": (round(gpu_prefill_tflops * 1e3 / p_gfs, 1)
+                                            if gpu_prefill_tflops else None),
+                        "sample": "64-token prefill chunk at prefix 4032, layers 0-11 (10 "
+                                  f"sliding, 2 global), all 4 sequences: {p_flops/1e9:.2f} "
+                                  "GFLOP of visible-pair work"},
+            "long_context": {"value": round(l_gbs, 3), "unit": "GB/s", "kind": "oracle",
+                             "seconds": round(l_dt, 2),
+                             "gpu_over_oracle": (round(gpu_long_gbs / l_gbs, 1)
+                                                 if gpu_long_gbs else None),
+                             "sample": "long-context ragged decode, layers 0 (sliding) and 5 "
+                                       f"(global), all 64 sequences: {l_bytes/1e9:.3f} GB of "
+                                       "KV"}}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -494,7 +599,36 @@ def main():
     if not args.no_prefill:
         for p in ((960, 4032) if args.main_only else (0, 960, 4032)):
             prefill[f"prefix_{p}"] = bench_prefill(p, args, stream)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(dec)
+    p4032 = prefill.get("prefix_4032")
+    cpu = None if args.no_cpu_baseline else cpu_baseline(
+        dec, p4032["tflops"] if p4032 else None, long_ctx["gbs"] if long_ctx else None)
+    prefill_line = None
+    if p4032:
+        prefill_line = {
+            "metric": "prefill TFLOP/s (4 x head_dim flops per visible query-key pair)",
+            "value": p4032["tflops"],
+            "unit": "TFLOP/s",
+            "frac": round(p4032["tflops"] / BF16_PEAK_TFLOPS, 4),
+            "ms_per_step": round(p4032["us_per_step"] / 1e3, 4),
+            "gflop_per_step": p4032["gflop_per_step"],
+            "workload": "12B-shaped 48-layer 64-token prefill chunk (40 sliding W1024 16q/8kv "
+                        "D256 + 8 global 16q/1kv D512 k_eq_v), B=4, prefix 4032",
+            "roofline": {
+                "kernel": PREFILL_KERNEL + " (global-layer prefill, prefix 4032)",
+                "bound": "mfma",
+                "achieved": p4032["global_layer_tflops"],
+                "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(p4032["global_layer_tflops"] / BF16_PEAK_TFLOPS, 4),
+                "us_per_launch": p4032["global_layer_us"],
+                "gflop_per_launch": p4032["global_layer_gflop"],
+            },
+            "sliding_layer_us": p4032["sliding_layer_us"],
+            "sliding_layer_kv_gbs": p4032["sliding_layer_kv_gbs"],
+        }
+        for k, v in prefill.items():
+            prefill_line[f"{k}_us_per_step"] = v["us_per_step"]
+            prefill_line[f"{k}_tflops"] = v["tflops"]
 
     wl = dec["wl"]
     dom = dec["dom"]
@@ -506,6 +640,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(dec["ms"], 4),
+        "ms_per_step_mean": round(dec["mean_ms"], 4),
+        "timing": "median of the timed replays (HIP events between replays)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -536,7 +672,8 @@ def main():
         "long_context_decode": long_ctx,
         "softcap_decode": capped,
         "small_decode": small,
-        "prefill": prefill,
+        "prefill": prefill_line,
+        "prefill_by_prefix": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -44,16 +44,25 @@ def test_prefill_flops_closed_form():
     assert sum(bench.prefill_flops(wl0, i) for i in range(wl0.n_layers)) == want0
 
 
+def test_prefill_kv_bytes_closed_form():
+    # prefix 4032: a sliding (sequence, KV head) reads keys 3009 .. 4095
+    # (1087 keys, K and V); a global one reads all 4096 keys once (k_eq_v)
+    wl = W.g12b_prefill(4032)
+    assert bench.prefill_kv_bytes(wl, 0) == 4 * 8 * 1087 * 256 * 2 * 2
+    assert bench.prefill_kv_bytes(wl, 5) == 4 * 1 * 4096 * 512 * 2
+
+
 def test_counter_traffic_only_for_the_profiled_source(tmp_path, monkeypatch):
     got = bench.counter_traffic(bench.DOMINANT_KERNEL)
     text = open(bench.COUNTER_SUMMARY).read()
-    import hashlib
-    src = hashlib.sha256(open(bench.KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
-    if f"kernels.hip sha256[:16]: {src}" in text:
+    hashes = bench.source_hashes()
+    if all(f"{n} sha256[:16]: {h}" in text for n, h in hashes.items()):
         assert got is not None and got > 0
     else:
         assert got is None
-    other = tmp_path / "kernels.hip"
-    other.write_bytes(open(bench.KERNEL_SOURCE, "rb").read() + b"\n// edited\n")
-    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(other))
-    assert bench.counter_traffic(bench.DOMINANT_KERNEL) is None
+    for attr, name in (("KERNEL_SOURCE", "kernels.hip"), ("PLAN_SOURCE", "plan.cpp")):
+        other = tmp_path / name
+        other.write_bytes(open(getattr(bench, attr), "rb").read() + b"\n// edited\n")
+        monkeypatch.setattr(bench, attr, str(other))
+        assert bench.counter_traffic(bench.DOMINANT_KERNEL) is None
+        monkeypatch.undo()
