@@ -178,98 +178,67 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
 // Stand-alone version for large decode merges (a kernel boundary separates
 // writer and reader, so ordinary loads see the partials).  A workgroup takes
 // R = max(64, D/4) / (D/4) rows; every thread owns one 4-dim slice of a row.
-// The sequence lengths and every (m, l) pair are fetched together, then the
-// partial outputs of up to 32 splits at once, so the merge costs two memory
-// round trips.
+// A thread reads its row's sequence length, then the (m, l) pairs and its
+// slices of the partial outputs of up to CH splits at once, all from its own
+// row's slots (indices clamped to the row's splits: repeats hit in cache),
+// and merges them in registers: two memory round trips, no LDS, no barrier.
 template <int D>
 __global__ __launch_bounds__(D / 4 > 64 ? D / 4 : 64) void merge_kernel(MergeArgs a) {
   constexpr int D4 = D / 4;
   constexpr int NT = D4 > 64 ? D4 : 64;
   constexpr int R = NT / D4;
-  constexpr int CH = 32;                                  // splits loaded per batch
-  constexpr int PER = (R * kMaxDecodeSplits + NT - 1) / NT;  // (m, l) pairs per thread
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  __shared__ float wgt[R][kMaxDecodeSplits];
-  __shared__ float lval[R][kMaxDecodeSplits];
-  __shared__ float s_inv[R];
-  __shared__ int s_used[R];
+  constexpr int CH = 16;  // splits per round trip
   const int tid = threadIdx.x;
-  const size_t row0 = (size_t)blockIdx.x * R;
-
-  // (m, l) of every split slot of the workgroup's rows, issued before the
-  // lengths that say which slots are in use
-  f32x2 mlv[PER];
+  const int r_me = tid / D4;  // R * D4 == NT
+  const int d = 4 * (tid - r_me * D4);
+  const int row = blockIdx.x * R + r_me;
+  if (row >= a.rows) return;
+  int L = a.seq_lens[row / a.n_q];
+  L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
+  const int lo = a.window > 0 ? max(0, L - a.window) : 0;
+  int n, f, e;
+  decode_split_range(lo, L, a.KB, a.blocks_per_split, 0, &n, &f, &e);
+  if (n <= 1) return;  // written by the decode kernel itself
+  n = min(n, a.n_splits);
+  const float* pml = a.part_ml + (size_t)row * a.n_splits * 2;
+  const float* po = a.part_o + (size_t)row * a.n_splits * D + d;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  float M = kNegInf, lsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n; s0 += CH) {
+    f32x2 ml[CH];
+    f32x4 v[CH];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int idx = tid + i * NT;
-    const int r = idx / a.n_splits;
-    if (r < R && row0 + r < (size_t)a.rows)
-      mlv[i] = *reinterpret_cast<const f32x2*>(a.part_ml + ((row0 + r) * a.n_splits +
-                                                            (idx - r * a.n_splits)) * 2);
-  }
-  if (tid < R) {
-    const size_t row = row0 + tid;
-    int n_used = 0;
-    if (row < (size_t)a.rows) {
-      const int bseq = (int)(row / a.n_q);
-      int L = a.seq_lens[bseq];
-      L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
-      const int lo = a.window > 0 ? max(0, L - a.window) : 0;
-      int f, e;
-      decode_split_range(lo, L, a.KB, a.blocks_per_split, 0, &n_used, &f, &e);
-      if (n_used <= 1) n_used = 0;  // written by the decode kernel itself
+    for (int i = 0; i < CH; ++i) {
+      const int si = min(s0 + i, n - 1);
+      ml[i] = *reinterpret_cast<const f32x2*>(pml + (size_t)si * 2);
+      v[i] = *reinterpret_cast<const f32x4*>(po + (size_t)si * D);
     }
-    s_used[tid] = n_used;
-  }
+    // out = sum_s w_s O_s / sum_s w_s l_s, w_s = 2^(m_s - max m) over the
+    // splits with keys, in split order; rescaled when a batch raises the max
+    float bm = M;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int idx = tid + i * NT;
-    const int r = idx / a.n_splits;
-    if (r < R && row0 + r < (size_t)a.rows) {
-      wgt[r][idx - r * a.n_splits] = mlv[i][0];
-      lval[r][idx - r * a.n_splits] = mlv[i][1];
+    for (int i = 0; i < CH; ++i)
+      if (s0 + i < n && ml[i][1] > 0.f) bm = fmaxf(bm, ml[i][0]);
+    if (bm != M) {
+      const float sc = fast_exp2(M - bm);  // 0 while nothing was added
+      acc *= sc;
+      lsum *= sc;
+      M = bm;
     }
-  }
-  __syncthreads();
-  if (tid < R && s_used[tid] > 0) {
-    const int n = s_used[tid];
-    float M = kNegInf;
-    for (int s = 0; s < n; ++s)
-      if (lval[tid][s] > 0.f) M = fmaxf(M, wgt[tid][s]);
-    float lsum = 0.f;
-    for (int s = 0; s < n; ++s) {
-      const float l = lval[tid][s];
-      const float w = l > 0.f ? fast_exp2(wgt[tid][s] - M) : 0.f;
-      wgt[tid][s] = w;
-      lsum += w * l;
-    }
-    s_inv[tid] = lsum > 0.f ? 1.f / lsum : 0.f;
-  }
-  __syncthreads();
-
-  for (int item = tid; item < R * D4; item += NT) {
-    const int r = item / D4;
-    const int d = 4 * (item - r * D4);
-    const int n = s_used[r];
-    const size_t row = row0 + r;
-    if (n == 0 || row >= (size_t)a.rows) continue;
-    const float* po = a.part_o + row * a.n_splits * D + d;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < n; s0 += CH) {
-      f32x4 v[CH];
 #pragma unroll
-      for (int i = 0; i < CH; ++i)
-        if (s0 + i < n) v[i] = *reinterpret_cast<const f32x4*>(po + (size_t)(s0 + i) * D);
-#pragma unroll
-      for (int i = 0; i < CH; ++i)
-        if (s0 + i < n && wgt[r][s0 + i] != 0.f) acc += wgt[r][s0 + i] * v[i];
-    }
-    const size_t out_off = row * D;
-    bf16x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = (__bf16)(acc[j] * s_inv[r]);
-    *reinterpret_cast<bf16x4*>(a.out + out_off + d) = o;
+    for (int i = 0; i < CH; ++i)
+      if (s0 + i < n && ml[i][1] > 0.f) {
+        const float w = fast_exp2(ml[i][0] - M);
+        lsum += w * ml[i][1];
+        acc += w * v[i];
+      }
   }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  bf16x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = (__bf16)(acc[j] * inv);
+  *reinterpret_cast<bf16x4*>(a.out + (size_t)row * D + d) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -918,7 +887,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
       }
     };
     if (!a.merge_in_kernel) {  // merge_kernel follows
-      publish(false);
+      publish(true);  // written through: less for the end-of-kernel write-back
       return;
     }
     // In-kernel merge: every split publishes its partial, waits for the
