@@ -30,6 +30,11 @@ constexpr int kPrefillRows = 16;
 
 // Keys per decode key block, on layers with and without a V plane.
 constexpr int kDecodeBlock = 32;
+// A decode call that reads more cache bytes than this streams them past the
+// caches (non-temporal loads): more than the eight XCDs' L2s hold together.
+// Smaller calls use the default policy, so that a small cache stays resident
+// from one step to the next.
+constexpr int64_t kStreamLoadBytes = int64_t(32) << 20;
 
 // Waves per SIMD an attention kernel instance is built for: 2 (up to 256
 // registers per lane), or 1 where one wave needs more (head_dim 512 without
@@ -109,6 +114,9 @@ struct DecodeArgs {
   // the same number of blocks whatever the sequence's length.
   int blocks_per_split, n_splits;
   int merge_in_kernel;  // 1: last arriving workgroup merges; 0: a merge kernel follows
+  // 1: cache rows are loaded with the non-temporal hint (the call reads more
+  // than kStreamLoadBytes); 0: default cache policy
+  int stream_loads;
   float scale_log2;     // scale * log2(e)
   // attention-logit cap c (softcap != 0): score * log2(e) =
   // cap_log2 * tanh(q.k * cap_in), cap_in = scale / c, cap_log2 = c * log2(e)

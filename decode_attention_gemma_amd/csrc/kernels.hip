@@ -81,11 +81,13 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-// Cache rows: decode reads each KV byte once per call, so its loads carry the
-// non-temporal hint (streamed past the caches; on a 134 MB layer this takes
-// the sustained read rate from about 5.8 to 6.3 TB/s).  Prefill rereads every
-// key block from L2 across the row blocks of one (sequence, KV head), so its
-// loads keep the default policy.
+// Cache rows: decode reads each KV byte once per call, so where a call reads
+// more than the caches hold its loads carry the non-temporal hint (streamed
+// past the caches; on a 134 MB layer this takes the sustained read rate from
+// about 5.8 to 6.3 TB/s).  Smaller calls keep the default policy, under which
+// a cache that fits stays resident from one step to the next.  Prefill
+// rereads every key block from L2 across the row blocks of one (sequence, KV
+// head), so its loads keep the default policy.
 template <bool NT>
 __device__ __forceinline__ u32x4 ldc16(const uint16_t* p) {
   if constexpr (NT)
@@ -300,7 +302,7 @@ struct Shape {
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D, bool KEQV, int NW, bool PREFILL, bool PAGED, bool CAP>
+template <int D, bool KEQV, int NW, bool PREFILL, bool PAGED, bool CAP, bool NTL>
 __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void attend_kernel(
     DecodeArgs da, PrefillArgs pa) {
   // k_eq_v prefill stages each K sub-tile for the V^T transpose as soon as
@@ -483,7 +485,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kreg[sb][s] = ldc16<!PREFILL>(kb + (sb * KS + s) * 512);
+      for (int s = 0; s < KS; ++s) kreg[sb][s] = ldc16<NTL>(kb + (sb * KS + s) * 512);
   };
   auto load_v = [&](int blk) {
     if constexpr (!KEQV) {
@@ -491,7 +493,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
       const uint16_t* vs = vp + seg_of(blk, slot0);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        vreg[db] = ldc16<!PREFILL>(vs + ((size_t)(slot0 / 32) * NDB + db) * 512 + lane * 8);
+        vreg[db] = ldc16<NTL>(vs + ((size_t)(slot0 / 32) * NDB + db) * 512 + lane * 8);
     }
   };
   const int n_mine = n_keys > 0 && blk_first + w < blk_end
@@ -587,7 +589,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
           *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[0][s];
           if (PFX) {
             asm volatile("" ::: "memory");  // after the staging write
-            kreg[0][s] = ldc16<!PREFILL>(kbn + s * 512);
+            kreg[0][s] = ldc16<NTL>(kbn + s * 512);
           }
         }
       }
@@ -728,7 +730,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
           for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
             for (int s = 0; s < S::TRH; ++s)
-              kreg[sb][ph * S::TRH + s] = ldc16<!PREFILL>(kbn + (sb * KS + ph * S::TRH + s) * 512);
+              kreg[sb][ph * S::TRH + s] = ldc16<NTL>(kbn + (sb * KS + ph * S::TRH + s) * 512);
         }
         if (!vfull) {
 #pragma unroll
@@ -962,25 +964,33 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
 }
 
 // one attend_kernel launch, with or without the logit cap
-template <int D, bool KEQV, int NW, bool PREFILL, bool PAGED>
+template <int D, bool KEQV, int NW, bool PREFILL, bool PAGED, bool NTL>
 void attend_launch(bool cap, dim3 grid, hipStream_t s, const DecodeArgs& da,
                    const PrefillArgs& pa) {
   if (cap)
-    hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, PREFILL, PAGED, true>), grid, dim3(NW * 64), 0,
-                       s, da, pa);
+    hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, PREFILL, PAGED, true, NTL>), grid,
+                       dim3(NW * 64), 0, s, da, pa);
   else
-    hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, PREFILL, PAGED, false>), grid, dim3(NW * 64),
-                       0, s, da, pa);
+    hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, PREFILL, PAGED, false, NTL>), grid,
+                       dim3(NW * 64), 0, s, da, pa);
 }
 
 template <int D, bool KEQV>
 hipError_t decode_launch(const DecodeArgs& a, int batch, hipStream_t s) {
   dim3 grid(a.n_splits, a.n_kv * a.n_hblk, batch);
   PrefillArgs none{};
-  if (a.pt.table)
-    attend_launch<D, KEQV, 4, false, true>(a.softcap != 0, grid, s, a, none);
-  else
-    attend_launch<D, KEQV, 4, false, false>(a.softcap != 0, grid, s, a, none);
+  const bool cap = a.softcap != 0;
+  if (a.pt.table) {
+    if (a.stream_loads)
+      attend_launch<D, KEQV, 4, false, true, true>(cap, grid, s, a, none);
+    else
+      attend_launch<D, KEQV, 4, false, true, false>(cap, grid, s, a, none);
+  } else {
+    if (a.stream_loads)
+      attend_launch<D, KEQV, 4, false, false, true>(cap, grid, s, a, none);
+    else
+      attend_launch<D, KEQV, 4, false, false, false>(cap, grid, s, a, none);
+  }
   return hipGetLastError();
 }
 
@@ -993,9 +1003,9 @@ hipError_t prefill_launch(const PrefillArgs& a, hipStream_t s) {
   dim3 grid(8 * ((n_log + 7) / 8));
   DecodeArgs none{};
   if (a.pt.table)
-    attend_launch<D, KEQV, NW, true, true>(a.softcap != 0, grid, s, none, a);
+    attend_launch<D, KEQV, NW, true, true, false>(a.softcap != 0, grid, s, none, a);
   else
-    attend_launch<D, KEQV, NW, true, false>(a.softcap != 0, grid, s, none, a);
+    attend_launch<D, KEQV, NW, true, false, false>(a.softcap != 0, grid, s, none, a);
   return hipGetLastError();
 }
 

@@ -507,6 +507,10 @@ int32_t decode_impl(const g4attn_stack* st, int32_t layer, const void* q, const 
                 &a.blocks_per_split, &a.n_splits);
   a.merge_in_kernel =
       (int64_t)a.n_splits * nh * d.head_dim * 4 <= kInKernelMergeBytes ? 1 : 0;
+  // cache bytes this call may read: the hint's keys of every (sequence, KV head)
+  const int64_t call_bytes = (int64_t)batch * d.n_kv_heads * keys_max * d.head_dim * 2 *
+                             (d.k_eq_v ? 1 : 2);
+  a.stream_loads = call_bytes > g4::kStreamLoadBytes ? 1 : 0;
   a.q = static_cast<const uint16_t*>(q);
   a.kp = reinterpret_cast<uint16_t*>(st->cache + p.k_off);
   a.vp = reinterpret_cast<uint16_t*>(st->cache + p.v_off);
