@@ -26,6 +26,7 @@ Also reported on the same line:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-prefill] [--copy-calib] [--main-only] [--long-context-only]
+                       [--read-probe]
 """
 
 from __future__ import annotations
@@ -431,6 +432,77 @@ def _host64(t):
     return t.to("cpu", torch.float64).numpy()
 
 
+def read_probe(args, stream):
+    """HBM streaming read rate (the practical bound for the decode kernels):
+    one read kernel (libg4probe.so, built beside the library) over 134 MB
+    regions, the sliding decode layer's bytes, each launch a different region
+    of a 4 GiB buffer so that nothing is left in the 256 MB MALL from the
+    previous launch, and over the whole buffer at once; plain and
+    non-temporal loads, several grid sizes; medians of HIP-event timings."""
+    import ctypes
+
+    import torch
+
+    from decode_attention_gemma_amd import build as B
+
+    if not os.path.exists(B.PROBE_LIB):
+        raise ImportError(f"{B.PROBE_LIB} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.g4probe_read.restype = ctypes.c_int
+    lib.g4probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    region = 134217728
+    total = 4 << 30
+    buf = torch.empty(total, dtype=torch.uint8, device="cuda")
+    buf.view(torch.int32).fill_(0x3c003c00)
+    sink = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    n_regions = total // region
+    res = {}
+    with torch.cuda.stream(stream):
+        for nt in (0, 1):
+            for n_wg in (256, 512, 1024, 2048):
+                times = []
+                for it in range(max(args.steps, 20) + 3):
+                    off = (it % n_regions) * region
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    rc = lib.g4probe_read(buf.data_ptr() + off, region, nt, n_wg, sink.data_ptr(),
+                                          ctypes.c_void_p(stream.cuda_stream))
+                    e1.record(stream)
+                    if rc != 0:
+                        raise RuntimeError(f"g4probe_read: hip error {rc}")
+                    e1.synchronize()
+                    if it >= 3:
+                        times.append(e0.elapsed_time(e1))
+                times.sort()
+                ms = times[len(times) // 2]
+                key = f"{'nt' if nt else 'plain'}_134MB_{n_wg}wg"
+                res[key] = round(region / (ms * 1e-3) / 1e9, 1)
+                log(f"[bench] read probe 134 MB regions, {'non-temporal' if nt else 'plain'} loads, "
+                    f"{n_wg} workgroups: {ms*1e3:.1f} us, {res[key]:.0f} GB/s")
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            times = []
+            for it in range(6):
+                e0.record(stream)
+                lib.g4probe_read(buf.data_ptr(), total, nt, 2048, sink.data_ptr(),
+                                 ctypes.c_void_p(stream.cuda_stream))
+                e1.record(stream)
+                e1.synchronize()
+                if it >= 1:
+                    times.append(e0.elapsed_time(e1))
+            times.sort()
+            ms = times[len(times) // 2]
+            key = f"{'nt' if nt else 'plain'}_4GiB_2048wg"
+            res[key] = round(total / (ms * 1e-3) / 1e9, 1)
+            log(f"[bench] read probe 4 GiB at once, {'non-temporal' if nt else 'plain'} loads: "
+                f"{ms*1e3:.0f} us, {res[key]:.0f} GB/s")
+    del buf, sink
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(dec, gpu_prefill_tflops=None, gpu_long_gbs=None):
     """The fp64 oracle, timed on the host cores on bounded samples of the
     benchmarked workloads (inputs are the same seeded bf16 tensors, copied to
@@ -556,6 +628,9 @@ def main():
     ap.add_argument("--long-context-only", action="store_true",
                     help="run only the long-context ragged decode stack and log its step time "
                          "(no JSON line; for per-kernel profiles of that workload)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="run only the HBM read-rate probe (plain and non-temporal loads) and "
+                         "log its rates (no JSON line)")
     ap.add_argument("--main-only", action="store_true",
                     help="skip the TP=2 rank stack, the fused-append step and the paged step, "
                          "which launch the decode kernels at other shapes or in other "
@@ -578,6 +653,9 @@ def main():
     stream = torch.cuda.Stream()
     if args.long_context_only:
         bench_long_decode(args, stream)
+        return
+    if args.read_probe:
+        read_probe(args, stream)
         return
     if args.copy_calib:
         src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")

@@ -1,4 +1,5 @@
-"""Build libg4attn.so (HIP kernels + C-ABI host code) for gfx950, in-tree."""
+"""Build libg4attn.so (HIP kernels + C-ABI host code) for gfx950, in-tree,
+and libg4probe.so, the HBM read-rate probe bench.py --read-probe uses."""
 
 from __future__ import annotations
 
@@ -10,6 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libg4attn.so")
+PROBE_LIB = os.path.join(HERE, "libg4probe.so")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
 HIP_FLAGS = [
@@ -35,6 +37,10 @@ def build_library(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([hipcc(), *HIP_FLAGS, "-shared", "-x", "hip", os.path.join(CSRC, "read_probe.hip"),
+          "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -66,3 +66,22 @@ def test_counter_traffic_only_for_the_profiled_source(tmp_path, monkeypatch):
         monkeypatch.setattr(bench, attr, str(other))
         assert bench.counter_traffic(bench.DOMINANT_KERNEL) is None
         monkeypatch.undo()
+
+
+def test_read_probe_library_exports_its_entry_point():
+    """The read-rate probe bench.py --read-probe times is built beside the
+    library and exports its one C entry point (no GPU call here)."""
+    import ctypes
+
+    from decode_attention_gemma_amd import build as B
+
+    if not os.path.exists(B.PROBE_LIB):
+        import pytest
+
+        pytest.skip("libg4probe.so not built")
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    assert hasattr(lib, "g4probe_read")
+    # the attention library's ABI does not carry it
+    from decode_attention_gemma_amd import g4attn
+
+    assert not hasattr(ctypes.CDLL(g4attn.LIB_PATH), "g4probe_read")
