@@ -180,10 +180,12 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
 // Stand-alone version for large decode merges (a kernel boundary separates
 // writer and reader, so ordinary loads see the partials).  A workgroup takes
 // R = max(64, D/4) / (D/4) rows; every thread owns one 4-dim slice of a row.
-// A thread reads its row's sequence length, then the (m, l) pairs and its
-// slices of the partial outputs of up to CH splits at once, all from its own
-// row's slots (indices clamped to the row's splits: repeats hit in cache),
-// and merges them in registers: two memory round trips, no LDS, no barrier.
+// A thread reads the (m, l) pairs and its slices of the partial outputs of up
+// to CH splits at once, all from its own row's slots, and merges them in
+// registers: no LDS, no barrier.  The first CH splits' loads go out together
+// with the sequence length (their addresses do not depend on it; slots past
+// the row's splits are read and ignored), so a row of at most CH splits
+// takes one memory round trip.
 template <int D>
 __global__ __launch_bounds__(D / 4 > 64 ? D / 4 : 64) void merge_kernel(MergeArgs a) {
   constexpr int D4 = D / 4;
@@ -195,6 +197,21 @@ __global__ __launch_bounds__(D / 4 > 64 ? D / 4 : 64) void merge_kernel(MergeArg
   const int d = 4 * (tid - r_me * D4);
   const int row = blockIdx.x * R + r_me;
   if (row >= a.rows) return;
+  const float* pml = a.part_ml + (size_t)row * a.n_splits * 2;
+  const float* po = a.part_o + (size_t)row * a.n_splits * D + d;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  f32x2 ml[CH];
+  f32x4 v[CH];
+  // splits s0 .. s0 + CH - 1, indices clamped to `last` (repeats hit in cache)
+  auto load_batch = [&](int s0, int last) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int si = min(s0 + i, last);
+      ml[i] = *reinterpret_cast<const f32x2*>(pml + (size_t)si * 2);
+      v[i] = *reinterpret_cast<const f32x4*>(po + (size_t)si * D);
+    }
+  };
+  load_batch(0, a.n_splits - 1);
   int L = a.seq_lens[row / a.n_q];
   L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
   const int lo = a.window > 0 ? max(0, L - a.window) : 0;
@@ -202,20 +219,10 @@ __global__ __launch_bounds__(D / 4 > 64 ? D / 4 : 64) void merge_kernel(MergeArg
   decode_split_range(lo, L, a.KB, a.blocks_per_split, 0, &n, &f, &e);
   if (n <= 1) return;  // written by the decode kernel itself
   n = min(n, a.n_splits);
-  const float* pml = a.part_ml + (size_t)row * a.n_splits * 2;
-  const float* po = a.part_o + (size_t)row * a.n_splits * D + d;
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
   float M = kNegInf, lsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < n; s0 += CH) {
-    f32x2 ml[CH];
-    f32x4 v[CH];
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int si = min(s0 + i, n - 1);
-      ml[i] = *reinterpret_cast<const f32x2*>(pml + (size_t)si * 2);
-      v[i] = *reinterpret_cast<const f32x4*>(po + (size_t)si * D);
-    }
+    if (s0 > 0) load_batch(s0, n - 1);
     // out = sum_s w_s O_s / sum_s w_s l_s, w_s = 2^(m_s - max m) over the
     // splits with keys, in split order; rescaled when a batch raises the max
     float bm = M;
