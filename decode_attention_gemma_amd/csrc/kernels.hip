@@ -908,8 +908,11 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
     if (!arrive_last(a.counters + grp, n_used, &s_flag)) return;
     // out = sum_s w_s O_s / sum_s w_s l_s, w_s = 2^(m_s - max m), splits in
     // index order (the result does not depend on which split arrived last);
-    // up to kBatch splits per memory round trip, rescaled between batches
-    constexpr int kBatch = 8;
+    // kBatch splits per memory round trip, rescaled between batches.  (A
+    // batch of 8, whose loads past the last split repeat the batch's first
+    // slot, measured slower on the two-split sliding layers: 25.5 against
+    // 25.2 us.  In-kernel merges hold at most kMaxInKernelSplits splits.)
+    constexpr int kBatch = 2;
     for (int idx = tid; idx < nrows * D4; idx += NT) {
       const int r = idx / D4;
       const int d = 4 * (idx - r * D4);

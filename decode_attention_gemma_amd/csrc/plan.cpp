@@ -120,8 +120,12 @@ void decode_splits(int keys_max, int KB, int pairs, int rows, int planes,
 }
 
 // Split results are merged by the last workgroup to arrive when the merge is
-// small; larger merges go to a separate kernel with one workgroup per row.
+// small (its partials within kInKernelMergeBytes, at most
+// kMaxInKernelSplits splits: that workgroup reads two splits per round
+// trip); larger merges go to a separate kernel with one thread per four
+// dims of a row, sixteen splits per round trip.
 constexpr int64_t kInKernelMergeBytes = 64 * 1024;
+constexpr int kMaxInKernelSplits = 8;
 
 }  // namespace
 
@@ -505,8 +509,10 @@ int32_t decode_impl(const g4attn_stack* st, int32_t layer, const void* q, const 
   const int KB = g4::kDecodeBlock;
   decode_splits(keys_max, KB, batch * d.n_kv_heads * n_hblk, nh, d.k_eq_v ? 1 : 2,
                 &a.blocks_per_split, &a.n_splits);
-  a.merge_in_kernel =
-      (int64_t)a.n_splits * nh * d.head_dim * 4 <= kInKernelMergeBytes ? 1 : 0;
+  a.merge_in_kernel = a.n_splits <= kMaxInKernelSplits &&
+                              (int64_t)a.n_splits * nh * d.head_dim * 4 <= kInKernelMergeBytes
+                          ? 1
+                          : 0;
   // cache bytes this call may read: the hint's keys of every (sequence, KV head)
   const int64_t call_bytes = (int64_t)batch * d.n_kv_heads * keys_max * d.head_dim * 2 *
                              (d.k_eq_v ? 1 : 2);

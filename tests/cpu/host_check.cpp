@@ -207,7 +207,7 @@ void check_decode_calls(const g4attn_stack* st, const std::vector<g4attn_layer_d
       if (n_used > a.n_splits) break;
     }
     if (a.merge_in_kernel)
-      CHECK((int64_t)a.n_splits * nh * c.head_dim * 4 <= 64 * 1024,
+      CHECK((int64_t)a.n_splits * nh * c.head_dim * 4 <= 64 * 1024 && a.n_splits <= 8,
             "%s: in-kernel merge of %d splits", what, a.n_splits);
     // workspace: counters, (m, l) and partials of every (row, split) slot
     const uint64_t base = kFakeBase + (1 << 20);
