@@ -26,7 +26,7 @@ Also reported on the same line:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-prefill] [--copy-calib] [--main-only] [--long-context-only]
-                       [--read-probe]
+                       [--read-probe] [--gemm-probe]
 """
 
 from __future__ import annotations
@@ -432,6 +432,24 @@ def _host64(t):
     return t.to("cpu", torch.float64).numpy()
 
 
+def probe_lib():
+    """libg4probe.so (the hardware-rate probes), built beside the library."""
+    import ctypes
+
+    from decode_attention_gemma_amd import build as B
+
+    if not os.path.exists(B.PROBE_LIB):
+        raise ImportError(f"{B.PROBE_LIB} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.g4probe_read.restype = ctypes.c_int
+    lib.g4probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    lib.g4probe_mfma.restype = ctypes.c_int
+    lib.g4probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
 def read_probe(args, stream):
     """HBM streaming read rate (the practical bound for the decode kernels):
     one read kernel (libg4probe.so, built beside the library) over 134 MB
@@ -443,14 +461,7 @@ def read_probe(args, stream):
 
     import torch
 
-    from decode_attention_gemma_amd import build as B
-
-    if not os.path.exists(B.PROBE_LIB):
-        raise ImportError(f"{B.PROBE_LIB} is not built; run __graft_entry__.build()")
-    lib = ctypes.CDLL(B.PROBE_LIB)
-    lib.g4probe_read.restype = ctypes.c_int
-    lib.g4probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
-                                 ctypes.c_void_p, ctypes.c_void_p]
+    lib = probe_lib()
     region = 134217728
     total = 4 << 30
     buf = torch.empty(total, dtype=torch.uint8, device="cuda")
@@ -499,6 +510,70 @@ def read_probe(args, stream):
             log(f"[bench] read probe 4 GiB at once, {'non-temporal' if nt else 'plain'} loads: "
                 f"{ms*1e3:.0f} us, {res[key]:.0f} GB/s")
     del buf, sink
+    torch.cuda.empty_cache()
+    return res
+
+
+def gemm_probe(args, stream):
+    """Achievable dense bf16 matrix-core rates, against the 2.5 PFLOP/s spec
+    figure: the issue rate of back-to-back 16x16x32 bf16 MFMAs with no memory
+    traffic (libg4probe.so, 256 workgroups, one or two waves per SIMD, 4 or 8
+    independent chains per wave), and large square bf16 GEMMs through
+    torch.matmul (the vendor BLAS, contiguous 2-D operands, fp32
+    accumulate).  Medians of HIP-event timings."""
+    import ctypes
+
+    import torch
+
+    lib = probe_lib()
+    res = {}
+    sink = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    iters = 4096
+    with torch.cuda.stream(stream):
+        for threads in (256, 512):
+            for chains in (4, 8):
+                times = []
+                for it in range(8):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    rc = lib.g4probe_mfma(256, threads, chains, iters, sink.data_ptr(),
+                                          ctypes.c_void_p(stream.cuda_stream))
+                    e1.record(stream)
+                    if rc != 0:
+                        raise RuntimeError(f"g4probe_mfma: hip error {rc}")
+                    e1.synchronize()
+                    if it >= 2:
+                        times.append(e0.elapsed_time(e1))
+                times.sort()
+                ms = times[len(times) // 2]
+                flops = 256 * (threads // 64) * iters * chains * 16 * 16 * 32 * 2
+                tf = flops / (ms * 1e-3) / 1e12
+                res[f"mfma_issue_{threads // 256}wps_{chains}ch"] = round(tf, 1)
+                log(f"[bench] mfma probe {threads // 256} wave(s) per SIMD, {chains} chains: "
+                    f"{ms*1e3:.0f} us, {tf:.0f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of spec)")
+        for n in (8192, 16384):
+            g = torch.Generator(device="cuda").manual_seed(7)
+            a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+            b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+            c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+            times = []
+            for it in range(max(args.steps, 20) + 3):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                torch.matmul(a, b, out=c)
+                e1.record(stream)
+                e1.synchronize()
+                if it >= 3:
+                    times.append(e0.elapsed_time(e1))
+            times.sort()
+            ms = times[len(times) // 2]
+            tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+            res[f"bf16_gemm_{n}"] = round(tf, 1)
+            log(f"[bench] gemm probe {n}x{n}x{n} bf16: {ms*1e3:.0f} us, {tf:.0f} TFLOP/s "
+                f"({tf / BF16_PEAK_TFLOPS:.1%} of the {BF16_PEAK_TFLOPS:.0f} TFLOP/s spec)")
+            del a, b, c
     torch.cuda.empty_cache()
     return res
 
@@ -631,6 +706,9 @@ def main():
     ap.add_argument("--read-probe", action="store_true",
                     help="run only the HBM read-rate probe (plain and non-temporal loads) and "
                          "log its rates (no JSON line)")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="run only the bf16 GEMM probe (the achievable matrix-core rate) and "
+                         "log its rates (no JSON line)")
     ap.add_argument("--main-only", action="store_true",
                     help="skip the TP=2 rank stack, the fused-append step and the paged step, "
                          "which launch the decode kernels at other shapes or in other "
@@ -656,6 +734,9 @@ def main():
         return
     if args.read_probe:
         read_probe(args, stream)
+        return
+    if args.gemm_probe:
+        gemm_probe(args, stream)
         return
     if args.copy_calib:
         src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")

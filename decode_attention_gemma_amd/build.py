@@ -1,5 +1,6 @@
 """Build libg4attn.so (HIP kernels + C-ABI host code) for gfx950, in-tree,
-and libg4probe.so, the HBM read-rate probe bench.py --read-probe uses."""
+and libg4probe.so, the hardware-rate probes bench.py --read-probe and
+--gemm-probe use."""
 
 from __future__ import annotations
 
@@ -38,7 +39,7 @@ def build_library(verbose: bool = False) -> str:
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     tmp = PROBE_LIB + ".tmp"
-    _run([hipcc(), *HIP_FLAGS, "-shared", "-x", "hip", os.path.join(CSRC, "read_probe.hip"),
+    _run([hipcc(), *HIP_FLAGS, "-shared", "-x", "hip", os.path.join(CSRC, "hw_probes.hip"),
           "-o", tmp], verbose)
     os.replace(tmp, PROBE_LIB)
     return LIB

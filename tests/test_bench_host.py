@@ -68,9 +68,10 @@ def test_counter_traffic_only_for_the_profiled_source(tmp_path, monkeypatch):
         monkeypatch.undo()
 
 
-def test_read_probe_library_exports_its_entry_point():
-    """The read-rate probe bench.py --read-probe times is built beside the
-    library and exports its one C entry point (no GPU call here)."""
+def test_probe_library_exports_its_entry_points():
+    """The hardware-rate probes bench.py --read-probe / --gemm-probe time are
+    built beside the library and export their C entry points (no GPU call
+    here)."""
     import ctypes
 
     from decode_attention_gemma_amd import build as B
@@ -80,8 +81,9 @@ def test_read_probe_library_exports_its_entry_point():
 
         pytest.skip("libg4probe.so not built")
     lib = ctypes.CDLL(B.PROBE_LIB)
-    assert hasattr(lib, "g4probe_read")
-    # the attention library's ABI does not carry it
+    assert hasattr(lib, "g4probe_read") and hasattr(lib, "g4probe_mfma")
+    # the attention library's ABI does not carry them
     from decode_attention_gemma_amd import g4attn
 
-    assert not hasattr(ctypes.CDLL(g4attn.LIB_PATH), "g4probe_read")
+    main = ctypes.CDLL(g4attn.LIB_PATH)
+    assert not hasattr(main, "g4probe_read") and not hasattr(main, "g4probe_mfma")
