@@ -98,7 +98,6 @@ __device__ __forceinline__ u32x4 ldc16(const uint16_t* p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-__device__ __forceinline__ __bf16 as_bf16(uint16_t x) { return __builtin_bit_cast(__bf16, x); }
 
 // Split partial results cross workgroups that may run on different XCDs
 // (each with its own L2).  They are written and read with the agent-scope
