@@ -42,6 +42,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kNegInf = -__builtin_huge_valf();
 // log2 of the largest probability the lazily rescaled online softmax admits
 constexpr float kLazyRescale = 8.f;
+// k_eq_v prefill: query sub-tiles read from LDS per wave ahead of the score
+// MFMA that uses them (one ahead; a second one makes the compiler spill)
+constexpr int kQueryReadAhead = 2;
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -53,6 +56,20 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lane groups that
+// hold one MFMA output column), with the VALU row swaps: no LDS round trip,
+// so it does not wait behind the wave's outstanding LDS operations.  After a
+// swap of x with itself, one of the two results holds the lane's own value
+// and the other its partner's.
+__device__ __forceinline__ float max_over_lane_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 // tanh for the attention-logit cap.  Below |x| = 1/16 its Taylor series
 // through x^7 (the next term is under 4e-13 relative there), so that a cap far
@@ -585,18 +602,30 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
       for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
         for (int c = 0; c < NCH; ++c) sch[sb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // k_eq_v prefill: query sub-tiles read QD - 1 ahead of their MFMA, so
+      // that more than one LDS read is in flight (the staging writes and
+      // compiler barriers below would otherwise leave one)
+      constexpr int QD = SAG ? kQueryReadAhead : 1;
+      bf16x8 qf[QD];
+#pragma unroll
+      for (int i = 0; i + 1 < QD; ++i)
+        qf[i] = *reinterpret_cast<const bf16x8*>(&Qs[(i * 64 + lane) * 8]);
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 qf = *reinterpret_cast<const bf16x8*>(&Qs[(s * 64 + lane) * 8]);
+        if (s + QD - 1 < KS)
+          qf[(s + QD - 1) % QD] =
+              *reinterpret_cast<const bf16x8*>(&Qs[((s + QD - 1) * 64 + lane) * 8]);
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb)
-          sch[sb][s % NCH] = mfma32(as_bf16x8(kreg[sb][s]), qf, sch[sb][s % NCH]);
+          sch[sb][s % NCH] = mfma32(as_bf16x8(kreg[sb][s]), qf[s % QD], sch[sb][s % NCH]);
         if constexpr (SAG) {
+          // Unconditional: without a next block `nxt` is this block again,
+          // an L2 hit.  Behind a run-time condition the compiler no longer
+          // counts these loads and, at the fifth sub-tile, waited for the
+          // next block's first loads as well: a memory round trip per block.
           *reinterpret_cast<u32x4*>(tr + s * 512 + lane * 8) = kreg[0][s];
-          if (PFX) {
-            asm volatile("" ::: "memory");  // after the staging write
-            kreg[0][s] = ldc16<NTL>(kbn + s * 512);
-          }
+          asm volatile("" ::: "memory");  // after the staging write
+          kreg[0][s] = ldc16<NTL>(kbn + s * 512);
         }
       }
 #pragma unroll
@@ -631,8 +660,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
         lmax = fmaxf(lmax, sacc[sb][j]);
       }
     }
-    lmax = fmaxf(lmax, __shfl_xor(lmax, 16));
-    lmax = fmaxf(lmax, __shfl_xor(lmax, 32));
+    if constexpr (PREFILL) {
+      // (decode keeps the shuffles: the row swaps measured no faster there)
+      lmax = max_over_lane_groups(lmax);
+    } else {
+      lmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+      lmax = fmaxf(lmax, __shfl_xor(lmax, 32));
+    }
     // Lazy rescaling: the reference max m_run moves only when some row's
     // block max exceeds it by more than 2^8, so probabilities stay <= 256
     // (exact enough in fp32 and bf16) and most blocks skip rescaling the
@@ -776,9 +810,10 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
   if (n_mine > 0) {
     int j = w;
     if constexpr (KEQV || D >= 512) {
-      // k_eq_v: no older load is waited for after the next block's loads
-      // are issued, so a run-time condition costs nothing.  head_dim 512 with
-      // a V plane: a second copy of the body does not fit the registers.
+      // k_eq_v decode: no older load is waited for after the next block's
+      // loads are issued, so a run-time condition costs nothing (k_eq_v
+      // prefill issues them unconditionally).  head_dim 512 with a V plane:
+      // a second copy of the body does not fit the registers.
       for (int i = 1; i <= n_mine; ++i, j += NW) block(phys(j), phys(i < n_mine ? j + NW : j), i < n_mine);
     } else {
       for (int i = 1; i < n_mine; ++i, j += NW) block(phys(j), phys(j + NW), std::true_type{});
