@@ -26,7 +26,7 @@ Also reported on the same line:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-prefill] [--copy-calib] [--main-only] [--long-context-only]
-                       [--read-probe] [--gemm-probe]
+                       [--read-probe] [--gemm-probe] [--delivery-probe]
 """
 
 from __future__ import annotations
@@ -447,7 +447,83 @@ def probe_lib():
     lib.g4probe_mfma.restype = ctypes.c_int
     lib.g4probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_void_p, ctypes.c_void_p]
+    lib.g4probe_lds.restype = ctypes.c_int
+    lib.g4probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_void_p, ctypes.c_void_p]
+    lib.g4probe_l2.restype = ctypes.c_int
+    lib.g4probe_l2.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     return lib
+
+
+def _median_launch_ms(stream, launch, reps):
+    """Median of `reps` HIP-event timings of launch() on `stream`, after one
+    untimed launch."""
+    import torch
+
+    times = []
+    for it in range(reps + 1):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = launch()
+        e1.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"probe launch: hip error {rc}")
+        e1.synchronize()
+        if it > 0:
+            times.append(e0.elapsed_time(e1))
+    times.sort()
+    return times[len(times) // 2]
+
+
+def delivery_probe(args, stream):
+    """Per-CU operand delivery, the bounds of the prefill kernels
+    (libg4probe.so): the LDS read rate of 16-byte and of transposing 8-byte
+    reads, and the L2 -> CU load rate into registers or straight into LDS,
+    with 4, 8 and 16 waves per CU (one workgroup on each of the 256 CUs).
+    Bytes per clock at the 2.4 GHz peak engine clock."""
+    import ctypes
+
+    import torch
+
+    lib = probe_lib()
+    sink = torch.zeros(1 << 14, dtype=torch.uint8, device="cuda")
+    cs = ctypes.c_void_p(stream.cuda_stream)
+    reps = max(args.steps, 10)
+    res = {}
+    n_cu, clk = 256, 2.4e9
+    with torch.cuda.stream(stream):
+        for tr in (0, 1):
+            for threads in (256, 512, 1024):
+                iters = 2048
+                ms = _median_launch_ms(stream, lambda: lib.g4probe_lds(
+                    tr, n_cu, threads, iters, sink.data_ptr(), cs), reps)
+                per_cu = (threads // 64) * iters * 4096 / (ms * 1e-3)
+                key = f"lds_{'tr_b64' if tr else 'b128'}_{threads // 64}w"
+                res[key] = round(per_cu / clk, 1)
+                log(f"[bench] lds probe {'ds_read_b64_tr_b16' if tr else 'ds_read_b128'}, "
+                    f"{threads // 64} waves per CU: {ms*1e3:.0f} us, {per_cu/1e9:.0f} GB/s per CU, "
+                    f"{per_cu/clk:.0f} B/clk")
+        for region in (256 << 10, 1 << 20):
+            buf = torch.zeros(8 * region, dtype=torch.uint8, device="cuda")
+            passes = (64 << 20) // region
+            for to_lds in (0, 1):
+                for threads in (256, 512, 1024):
+                    ms = _median_launch_ms(stream, lambda: lib.g4probe_l2(
+                        to_lds, buf.data_ptr(), region, n_cu, threads, passes, sink.data_ptr(),
+                        cs), reps)
+                    per_cu = region * passes / (ms * 1e-3)
+                    key = f"l2_{region >> 10}KiB_{'lds' if to_lds else 'vgpr'}_{threads // 64}w"
+                    res[key] = round(per_cu / 1e9, 1)
+                    log(f"[bench] l2 probe {region >> 10} KiB per XCD, "
+                        f"{'into LDS' if to_lds else 'into registers'}, {threads // 64} waves per "
+                        f"CU: {ms*1e3:.0f} us, {per_cu/1e9:.0f} GB/s per CU ({per_cu/clk:.0f} "
+                        f"B/clk), {n_cu * per_cu / 1e12:.1f} TB/s in all")
+            del buf
+    del sink
+    torch.cuda.empty_cache()
+    return res
 
 
 def read_probe(args, stream):
@@ -706,6 +782,9 @@ def main():
     ap.add_argument("--read-probe", action="store_true",
                     help="run only the HBM read-rate probe (plain and non-temporal loads) and "
                          "log its rates (no JSON line)")
+    ap.add_argument("--delivery-probe", action="store_true",
+                    help="run only the LDS and L2 -> CU delivery probes (the prefill kernels' "
+                         "operand paths) and exit")
     ap.add_argument("--gemm-probe", action="store_true",
                     help="run only the bf16 GEMM probe (the achievable matrix-core rate) and "
                          "log its rates (no JSON line)")
@@ -737,6 +816,9 @@ def main():
         return
     if args.gemm_probe:
         gemm_probe(args, stream)
+        return
+    if args.delivery_probe:
+        delivery_probe(args, stream)
         return
     if args.copy_calib:
         src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")

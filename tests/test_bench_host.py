@@ -69,9 +69,9 @@ def test_counter_traffic_only_for_the_profiled_source(tmp_path, monkeypatch):
 
 
 def test_probe_library_exports_its_entry_points():
-    """The hardware-rate probes bench.py --read-probe / --gemm-probe time are
-    built beside the library and export their C entry points (no GPU call
-    here)."""
+    """The hardware-rate probes bench.py --read-probe / --gemm-probe /
+    --delivery-probe time are built beside the library and export their C
+    entry points (no GPU call here)."""
     import ctypes
 
     from decode_attention_gemma_amd import build as B
@@ -81,9 +81,10 @@ def test_probe_library_exports_its_entry_points():
 
         pytest.skip("libg4probe.so not built")
     lib = ctypes.CDLL(B.PROBE_LIB)
-    assert hasattr(lib, "g4probe_read") and hasattr(lib, "g4probe_mfma")
+    names = ("g4probe_read", "g4probe_mfma", "g4probe_lds", "g4probe_l2")
+    assert all(hasattr(lib, n) for n in names)
     # the attention library's ABI does not carry them
     from decode_attention_gemma_amd import g4attn
 
     main = ctypes.CDLL(g4attn.LIB_PATH)
-    assert not hasattr(main, "g4probe_read") and not hasattr(main, "g4probe_mfma")
+    assert not any(hasattr(main, n) for n in names)
