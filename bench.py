@@ -58,8 +58,8 @@ def kv_bytes(wl, layer):
     return keys * d.n_kv_heads * d.head_dim * 2 * (1 if d.k_eq_v else 2)
 
 
-DOMINANT_KERNEL = "attend_kernel<256, false, 4, false, false, false, true>"
-PREFILL_KERNEL = "attend_kernel<512, true, 8, true, false, false, false>"
+DOMINANT_KERNEL = "attend_kernel<256, false, 4, false, false, false, true, false>"
+PREFILL_KERNEL = "attend_kernel<512, true, 8, true, false, false, false, false>"
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "attend_12b_hbm_bytes.md")
 KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_gemma_amd", "csrc", "kernels.hip")
 PLAN_SOURCE = os.path.join(ROOT, "decode_attention_gemma_amd", "csrc", "plan.cpp")

@@ -325,9 +325,13 @@ struct Shape {
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D, bool KEQV, int NW, bool PREFILL, bool PAGED, bool CAP, bool NTL>
+// FUSED: the decode step that first writes the current token's K/V rows into
+// the cache (g4attn_decode_append); its own instances, so that the plain
+// decode carries none of that code.
+template <int D, bool KEQV, int NW, bool PREFILL, bool PAGED, bool CAP, bool NTL, bool FUSED>
 __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void attend_kernel(
     DecodeArgs da, PrefillArgs pa) {
+  static_assert(!(FUSED && PREFILL), "the token append is a decode step");
   // k_eq_v prefill stages each K sub-tile for the V^T transpose as soon as
   // its score MFMA has read it, and reloads the register with the next
   // block's sub-tile at once (a whole block of prefetch distance; the staging
@@ -407,7 +411,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
     full_hi = r_end;
     row_lo = r_beg;
     row_hi = r_end;
-    if (a.k_new != nullptr && L > 0 && r_end == L) new_pos = L - 1;
+    if (FUSED && L > 0 && r_end == L) new_pos = L - 1;
   } else {
     const PrefillArgs& a = pa;
     // physical workgroup p runs on XCD p % 8; give each XCD a contiguous
@@ -521,27 +525,56 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
   };
   const int n_mine = n_keys > 0 && blk_first + w < blk_end
                          ? (blk_end - (blk_first + w) + NW - 1) / NW : 0;  // blocks of this wave
-  if constexpr (!PREFILL) {
-    // Fused append: the wave that will read the current token's block writes
-    // the token's K (and V) row into its cache slot and waits for the stores
-    // before loading anything, so its loads see the row.  No other workgroup
-    // of this launch reads that slot as a visible key.  (Several head blocks
-    // of one KV head write the same bytes.)  The slot's segment is the
+  // fused append: this wave wrote the token's rows and must see its stores
+  // complete before the workgroup barrier below
+  bool wrote_row = false;
+  if constexpr (FUSED) {
+    // Fused append: the current token's K (and V) row is written into its
+    // cache slot before the wave that reads the token's block (the last block
+    // of the range) loads it.  When that block is the reading wave's first,
+    // whose loads are issued before the workgroup barrier below, the reader
+    // writes the row and waits for its stores before loading anything.
+    // Otherwise the next wave writes it and waits for its stores just before
+    // the barrier, while its own first block is in flight; the reader loads
+    // the token's block after the barrier, late in its stream.  (When the
+    // reader wrote and waited every time, the reader, which also streams the
+    // most blocks, started its stream a store round trip late.)  No other
+    // workgroup of this launch reads that slot as a visible key; several head
+    // blocks of one KV head write the same bytes.  The slot's segment is the
     // unpaged one or the page the block table maps the position to.
-    if (new_pos >= 0 && w == (new_pos / KB - blk_first) % NW) {
+    const int tok_j = new_pos / KB - blk_first;  // the token block's place in the range
+    const int writer = tok_j < NW ? tok_j : (tok_j + 1) % NW;
+    if (new_pos >= 0 && w == writer) {
       int slot0;
       const size_t sg = seg_of(new_pos / KB, slot0);
       const int slot = slot0 + new_pos % KB;
       const size_t row = ((size_t)b * n_kv + g) * D;
-      uint16_t* kdst = da.kp + sg;
-      for (int c = lane; c < D / 8; c += 64)
-        *reinterpret_cast<u32x4*>(kdst + k_elem_offset(slot, 8 * c, D) / 2) =
-            ldg16(da.k_new + row + 8 * c);
+      // Both rows are loaded before either is stored: one memory round trip.
+      // (Loaded and stored element by element, each load stayed behind the
+      // store before it, since the two may alias: four round trips.)  Lane l
+      // stores the V elements of dims l, l + 64, ...: the 8 lanes that share
+      // a 128-byte line of the V plane store in one instruction.
+      constexpr int NV = (D + 63) / 64;
+      const bool has_k = lane < D / 8;
+      u32x4 kc = {0u, 0u, 0u, 0u};
+      uint16_t vv[NV];
+      if (has_k) kc = ldg16(da.k_new + row + 8 * lane);
+      if constexpr (!KEQV) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          if (lane + 64 * i < D) vv[i] = da.v_new[row + lane + 64 * i];
+      }
+      if (has_k) *reinterpret_cast<u32x4*>(da.kp + sg + k_elem_offset(slot, 8 * lane, D) / 2) = kc;
       if constexpr (!KEQV) {
         uint16_t* vdst = da.vp + sg;
-        for (int d = lane; d < D; d += 64) vdst[v_elem_offset(slot, d, D) / 2] = da.v_new[row + d];
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          if (lane + 64 * i < D) vdst[v_elem_offset(slot, lane + 64 * i, D) / 2] = vv[i];
       }
-      wait_vmem();
+      if (tok_j < NW)
+        wait_vmem();
+      else
+        wrote_row = true;
     }
   }
   // block of the wave's j-th position in the range (j = w, w + NW, ...)
@@ -560,6 +593,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
   // compiler's wait for the queries would have to cover every load.
   load_k(phys(n_mine > 0 ? w : 0));
   load_v(phys(n_mine > 0 ? w : 0));
+  if (wrote_row) {
+    // everything older than the first block's loads, the token's row stores
+    // included, has landed (vector memory operations complete in issue order)
+    constexpr int n_first = NSB * KS + (KEQV ? 0 : NDB);
+    constexpr int vm = n_first < 63 ? n_first : 63;
+    __builtin_amdgcn_s_waitcnt((vm & 15) | ((vm >> 4) << 14) | 0x0F70);
+  }
 
   // queries as the B operand of S^T = K Q^T (column c16 = row, k-slots =
   // dims), kept in LDS in operand order: sub-tile s, lane L at (s*64 + L)*8
@@ -1008,33 +1048,41 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
 }
 
 // one attend_kernel launch, with or without the logit cap
-template <int D, bool KEQV, int NW, bool PREFILL, bool PAGED, bool NTL>
+template <int D, bool KEQV, int NW, bool PREFILL, bool PAGED, bool NTL, bool FUSED = false>
 void attend_launch(bool cap, dim3 grid, hipStream_t s, const DecodeArgs& da,
                    const PrefillArgs& pa) {
   if (cap)
-    hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, PREFILL, PAGED, true, NTL>), grid,
+    hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, PREFILL, PAGED, true, NTL, FUSED>), grid,
                        dim3(NW * 64), 0, s, da, pa);
   else
-    hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, PREFILL, PAGED, false, NTL>), grid,
+    hipLaunchKernelGGL((attend_kernel<D, KEQV, NW, PREFILL, PAGED, false, NTL, FUSED>), grid,
                        dim3(NW * 64), 0, s, da, pa);
+}
+
+template <int D, bool KEQV, bool FUSED>
+void decode_launch_as(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  PrefillArgs none{};
+  const bool cap = a.softcap != 0;
+  if (a.pt.table) {
+    if (a.stream_loads)
+      attend_launch<D, KEQV, 4, false, true, true, FUSED>(cap, grid, s, a, none);
+    else
+      attend_launch<D, KEQV, 4, false, true, false, FUSED>(cap, grid, s, a, none);
+  } else {
+    if (a.stream_loads)
+      attend_launch<D, KEQV, 4, false, false, true, FUSED>(cap, grid, s, a, none);
+    else
+      attend_launch<D, KEQV, 4, false, false, false, FUSED>(cap, grid, s, a, none);
+  }
 }
 
 template <int D, bool KEQV>
 hipError_t decode_launch(const DecodeArgs& a, int batch, hipStream_t s) {
   dim3 grid(a.n_splits, a.n_kv * a.n_hblk, batch);
-  PrefillArgs none{};
-  const bool cap = a.softcap != 0;
-  if (a.pt.table) {
-    if (a.stream_loads)
-      attend_launch<D, KEQV, 4, false, true, true>(cap, grid, s, a, none);
-    else
-      attend_launch<D, KEQV, 4, false, true, false>(cap, grid, s, a, none);
-  } else {
-    if (a.stream_loads)
-      attend_launch<D, KEQV, 4, false, false, true>(cap, grid, s, a, none);
-    else
-      attend_launch<D, KEQV, 4, false, false, false>(cap, grid, s, a, none);
-  }
+  if (a.k_new)
+    decode_launch_as<D, KEQV, true>(a, grid, s);
+  else
+    decode_launch_as<D, KEQV, false>(a, grid, s);
   return hipGetLastError();
 }
 
