@@ -370,6 +370,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
   // prefill only
   int row0 = 0, t_row = 0, h_row = 0;
   int rot = 0;  // this row block's offset into its block range
+  int pg_row = 0;  // paged decode: block-table entry `tid` of the sequence
   // This wave's share of the query operand (sub-tiles w, w + NW, ...),
   // loaded before anything that depends on the sequence lengths or
   // positions: it is then in flight during the length read instead of queued
@@ -400,6 +401,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
     row_ok = c16 < nrows;
     qrow = a.q + ((size_t)b * a.n_q + head0 + c16) * D;
     load_q();
+    if constexpr (PAGED && !FUSED) {
+      // a block-table row of at most one entry per thread is loaded whole,
+      // with the queries: its address does not depend on the length.  (The
+      // fused step keeps the copy below: there this measured slower.)
+      if (a.pt.stride <= NT && tid < a.pt.stride)
+        pg_row = a.pt.table[(size_t)b * a.pt.stride + tid];
+    }
     int L = a.seq_lens[b];
     L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
     const int lo = a.window > 0 ? max(0, L - a.window) : 0;
@@ -472,8 +480,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
     const int pg_last = blk_end > blk_first ? (blk_end * KB - 1) / pt.page : pg_first;
     const int n_pg = min(pg_last - pg_first + 1, kMaxWgPages);
     const int32_t* row = pt.table + (size_t)b * pt.stride;
-    for (int i = tid; i < n_pg; i += NW * 64)
-      pg_ids[i] = clamp_page(row[min(pg_first + i, pt.stride - 1)], pt.n_pages);
+    if (!PREFILL && !FUSED && pt.stride <= NT) {  // the row loaded with the queries
+      const int i = tid - pg_first;
+      if (tid < pt.stride && i >= 0 && i < n_pg) pg_ids[i] = clamp_page(pg_row, pt.n_pages);
+    } else {
+      for (int i = tid; i < n_pg; i += NW * 64)
+        pg_ids[i] = clamp_page(row[min(pg_first + i, pt.stride - 1)], pt.n_pages);
+    }
     __syncthreads();
   }
   // element offset of the segment holding key block blk, and the block's
