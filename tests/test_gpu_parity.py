@@ -651,6 +651,9 @@ FUSED_GRID = [
     (12, 4, 64, 16, 1, [1, 16, 40, 95], 256, 16),
     (4, 2, 64, 8, 0, [1, 8, 64, 65, 200], 256, 16),   # ring of 64 slots wraps
     (32, 1, 64, 0, 0, [3, 200, 513], 1024, 64),         # two head blocks
+    # 16 sequences x 8 KV heads: two 17-block splits per (sequence, KV head),
+    # so a wave other than the token block's reader writes the token's rows
+    (16, 8, 256, 1024, 0, [1024 + 61 * i for i in range(16)], 2048, 64),
 ]
 
 
@@ -695,6 +698,7 @@ def test_fused_decode_step_equals_append_then_decode(nq, nkv, D, window, keqv, l
     (16, 1, 512, 0, 1, [1, 16, 17, 700, 2049], 4096, 64, 128),
     (12, 4, 64, 16, 1, [1, 16, 40, 95], 256, 16, 64),
     (32, 1, 64, 0, 0, [3, 200, 513], 1024, 64, 192),
+    (16, 8, 256, 1024, 0, [1024 + 61 * i for i in range(16)], 2048, 64, 64),
 ])
 def test_paged_fused_decode_step_equals_append_then_decode(nq, nkv, D, window, keqv, lens,
                                                            kv_max, max_chunk, page):
