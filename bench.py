@@ -344,16 +344,17 @@ def bench_softcap_decode(args, stream):
 
 
 def bench_paged_decode(args, stream):
-    """The 12B decode step through a paged cache: 64-slot pages in a seeded
-    random order over a pool of arbitrary bits, one block table for all
-    layers."""
+    """The 12B decode step through a paged cache: pages of `--page-size`
+    slots (64 by default) in a seeded random order over a pool of arbitrary
+    bits, one block table for all layers."""
     import torch
 
     from decode_attention_gemma_amd import harness as H, workloads as W
 
     wl = W.g12b_decode()
-    log(f"[bench] setup {wl.name} (paged cache, 64-slot pages)")
-    st = H.make_paged_stack(wl, page_size=64, device="cuda")
+    page = args.page_size
+    log(f"[bench] setup {wl.name} (paged cache, {page}-slot pages)")
+    st = H.make_paged_stack(wl, page_size=page, device="cuda")
     H.fill_cache(st, wl, "cuda")
     bufs = H.StepBuffers(wl, "cuda")
     g = graph_of(lambda: H.run_step(st, bufs, stream=stream.cuda_stream), stream)
@@ -381,7 +382,7 @@ def bench_paged_decode(args, stream):
         f"with the fused token append {ms_fus*1e3:.1f} us")
     del st, bufs, g
     torch.cuda.empty_cache()
-    return {"workload": wl.name + ", paged (64-slot pages, permuted)",
+    return {"workload": wl.name + f", paged ({page}-slot pages, permuted)",
             "us_per_step": round(ms * 1e3, 2), "gbs": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "fused_decode_append_us": round(ms_fus * 1e3, 2)}
@@ -788,6 +789,11 @@ def main():
     ap.add_argument("--gemm-probe", action="store_true",
                     help="run only the bf16 GEMM probe (the achievable matrix-core rate) and "
                          "log its rates (no JSON line)")
+    ap.add_argument("--paged-only", action="store_true",
+                    help="run only the 12B decode step, unpaged and through the paged cache, "
+                         "and log both times (no JSON line; for the paged layout's profiles)")
+    ap.add_argument("--page-size", type=int, default=64,
+                    help="slots per page of the paged decode step (a multiple of 64)")
     ap.add_argument("--main-only", action="store_true",
                     help="skip the TP=2 rank stack, the fused-append step and the paged step, "
                          "which launch the decode kernels at other shapes or in other "
@@ -810,6 +816,10 @@ def main():
     stream = torch.cuda.Stream()
     if args.long_context_only:
         bench_long_decode(args, stream)
+        return
+    if args.paged_only:
+        bench_decode(args, stream)
+        bench_paged_decode(args, stream)
         return
     if args.read_probe:
         read_probe(args, stream)

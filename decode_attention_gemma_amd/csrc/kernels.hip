@@ -381,8 +381,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
       const int s = w + i * NW;
+      // Decode: unconditional, since after a conditional load the compiler
+      // cannot count the loads in flight, and its later waits would cover
+      // the queries too.  Lanes past the last row read a valid row; each row
+      // is its own column of the MFMAs and only valid rows are written out.
+      // (Prefill keeps zeros there: the unconditional form spills.)
       if (QPW * NW == KS || s < KS)
-        qv[i] = row_ok ? ldg16(qrow + 32 * s + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+        qv[i] = PREFILL && !row_ok ? u32x4{0u, 0u, 0u, 0u} : ldg16(qrow + 32 * s + 8 * q4);
     }
   };
   if constexpr (!PREFILL) {
@@ -399,15 +404,16 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
     head0 = g * a.G + hblk * 16;
     nrows = min(16, a.G - hblk * 16);
     row_ok = c16 < nrows;
-    qrow = a.q + ((size_t)b * a.n_q + head0 + c16) * D;
-    load_q();
+    qrow = a.q + ((size_t)b * a.n_q + head0 + (row_ok ? c16 : 0)) * D;
     if constexpr (PAGED && !FUSED) {
       // a block-table row of at most one entry per thread is loaded whole,
-      // with the queries: its address does not depend on the length.  (The
-      // fused step keeps the copy below: there this measured slower.)
-      if (a.pt.stride <= NT && tid < a.pt.stride)
-        pg_row = a.pt.table[(size_t)b * a.pt.stride + tid];
+      // before the queries: its address does not depend on the length, and
+      // the waits for it then leave the queries in flight (loads complete in
+      // issue order).  (The fused step keeps the copy below: there this
+      // measured slower.)
+      pg_row = a.pt.table[(size_t)b * a.pt.stride + min(tid, a.pt.stride - 1)];
     }
+    load_q();
     int L = a.seq_lens[b];
     L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
     const int lo = a.window > 0 ? max(0, L - a.window) : 0;
@@ -480,6 +486,11 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
     const int pg_last = blk_end > blk_first ? (blk_end * KB - 1) / pt.page : pg_first;
     const int n_pg = min(pg_last - pg_first + 1, kMaxWgPages);
     const int32_t* row = pt.table + (size_t)b * pt.stride;
+    // The row's load (issued whatever the row's size) is waited for here, on
+    // every path: otherwise the compiler, which merges what it knows of both
+    // paths, waits for it again after the barrier below, together with
+    // every load issued after it.
+    if constexpr (!PREFILL && !FUSED) asm volatile("" ::"v"(pg_row));
     if (!PREFILL && !FUSED && pt.stride <= NT) {  // the row loaded with the queries
       const int i = tid - pg_first;
       if (tid < pt.stride && i >= 0 && i < n_pg) pg_ids[i] = clamp_page(pg_row, pt.n_pages);
