@@ -801,6 +801,26 @@ def test_paged_ragged_lengths_against_oracle():
         check_close(bufs.out[i], ref, f"paged ragged layer {i}")
 
 
+def test_paged_block_table_wider_than_a_workgroup():
+    """Block-table rows of 320 entries (20480 positions, 64-slot pages), wider
+    than the 256 threads that hold one entry each on the narrow-row path: the
+    decode copies the page ids through its loop instead.  Bit-identical to the
+    unpaged stack, and against the oracle on every sequence."""
+    layers = [_desc(4, 2, 64, window=100), _desc(8, 1, 128, keqv=1)]
+    lens = [20000, 300, 17001]
+    wl = W.Workload(cfg_id=91, name="paged wide table", kind="decode", layers=layers,
+                    batch=len(lens), kv_max=20480, max_chunk=64, seq_lens=lens, start_pos=None,
+                    n_tok=1)
+    _, ref = run_workload(wl)
+    pst, got = _run_paged(wl, 64)
+    assert pst.block_table.shape[1] == 320
+    for i in range(len(layers)):
+        assert torch.equal(got.out[i], ref.out[i]), f"wide table layer {i}: paged != unpaged"
+        q = f64(got.q[i])
+        want = np.stack([oracle_decode(wl, i, b, q) for b in range(wl.batch)])
+        check_close(got.out[i], want, f"paged wide table layer {i}")
+
+
 def test_length_beyond_hint_is_clamped_and_leaves_no_state():
     """seq_lens above the max_seq_len hint: the kernels treat them as the hint,
     so the call covers only the planned splits, every arrival counter returns
