@@ -405,12 +405,11 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
     nrows = min(16, a.G - hblk * 16);
     row_ok = c16 < nrows;
     qrow = a.q + ((size_t)b * a.n_q + head0 + (row_ok ? c16 : 0)) * D;
-    if constexpr (PAGED && !FUSED) {
+    if constexpr (PAGED) {
       // a block-table row of at most one entry per thread is loaded whole,
       // before the queries: its address does not depend on the length, and
       // the waits for it then leave the queries in flight (loads complete in
-      // issue order).  (The fused step keeps the copy below: there this
-      // measured slower.)
+      // issue order).
       pg_row = a.pt.table[(size_t)b * a.pt.stride + min(tid, a.pt.stride - 1)];
     }
     load_q();
@@ -490,8 +489,8 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(D, KEQV, PREFILL)) void att
     // every path: otherwise the compiler, which merges what it knows of both
     // paths, waits for it again after the barrier below, together with
     // every load issued after it.
-    if constexpr (!PREFILL && !FUSED) asm volatile("" ::"v"(pg_row));
-    if (!PREFILL && !FUSED && pt.stride <= NT) {  // the row loaded with the queries
+    if constexpr (!PREFILL) asm volatile("" ::"v"(pg_row));
+    if (!PREFILL && pt.stride <= NT) {  // the row loaded with the queries
       const int i = tid - pg_first;
       if (tid < pt.stride && i >= 0 && i < n_pg) pg_ids[i] = clamp_page(pg_row, pt.n_pages);
     } else {
