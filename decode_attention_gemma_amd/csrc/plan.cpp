@@ -98,9 +98,10 @@ int32_t check_layer(const g4attn_stack* st, int32_t layer) {
 // A split also gets at least one block per wave where the context has them.
 // (Planning k_eq_v layers for more, shorter splits or fewer, longer ones
 // measured slower in both directions.)
-void decode_splits(int keys_max, int KB, int pairs, int rows, int planes,
+void decode_splits(int keys_max, int KB, int pairs, int rows, int planes, bool aligned_start,
                    int* blocks_per_split, int* n_splits) {
-  const int nb_max = (keys_max + KB - 1) / KB + 1;  // +1: alignment of the first block
+  // a range that may start inside a block spans one block more
+  const int nb_max = (keys_max + KB - 1) / KB + (aligned_start ? 0 : 1);
   const int target_wgs = 256;
   int ns = ceil_div(target_wgs, pairs);
   if (ns > g4::kMaxDecodeSplits) ns = g4::kMaxDecodeSplits;
@@ -507,7 +508,9 @@ int32_t decode_impl(const g4attn_stack* st, int32_t layer, const void* q, const 
   const int keys_max = d.window > 0 && d.window < max_seq_len ? d.window : max_seq_len;
   g4::DecodeArgs a;
   const int KB = g4::kDecodeBlock;
-  decode_splits(keys_max, KB, batch * d.n_kv_heads * n_hblk, nh, d.k_eq_v ? 1 : 2,
+  // key ranges start at 0 (a block edge) unless a window can move their start
+  const bool aligned_start = d.window == 0 || d.window >= max_seq_len;
+  decode_splits(keys_max, KB, batch * d.n_kv_heads * n_hblk, nh, d.k_eq_v ? 1 : 2, aligned_start,
                 &a.blocks_per_split, &a.n_splits);
   a.merge_in_kernel = a.n_splits <= kMaxInKernelSplits &&
                               (int64_t)a.n_splits * nh * d.head_dim * 4 <= kInKernelMergeBytes
